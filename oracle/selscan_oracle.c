@@ -1,0 +1,157 @@
+/*
+ * CPU oracle for the S6 selective scan -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the bench's CPU-baseline leg may
+ * load this code.  The HIP library shares nothing with it: no headers, no
+ * helpers, no constants.
+ *
+ * It is the plain definition of what the method computes, written out as a
+ * sequential loop in double precision:
+ *
+ *   delta_t = softplus(Delta_raw[b,t,d] + bias[d])     (or the raw sum when
+ *                                                       softplus is off)
+ *   for every state n:
+ *     h[n] = exp(delta_t * A[d,n]) * h[n] + delta_t * B[b,t,n] * u[b,t,d]
+ *   y[b,t,d] = sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]
+ *   y[b,t,d] *= z * sigmoid(z)                         (only when z is given)
+ *
+ * Sources, by page and section:
+ *  - Mamba tutorial (pwwt.cn), §2.2: zero-order hold gives A_bar = exp(Delta A);
+ *    in practice B_bar is simplified to Delta * B.
+ *  - same page, §3.1 and the Gu & Dao deep-reading report (zako-mio.github.io),
+ *    §2.3: B, C and Delta are functions of the input; Delta passes through
+ *    softplus; A stays input-independent.
+ *  - same tutorial, §4.2 listing: h starts at zero; each step updates h and
+ *    then reads it out with C_t; the skip term x*D is added to the scan output
+ *    and the result is multiplied by SiLU(z); B_t and C_t are broadcast over
+ *    the channel axis, A has one row per channel.
+ *  - same tutorial, §5.1 table and §6.3: decode keeps one fixed-size state per
+ *    sample and advances it by O(1) work per token.
+ *
+ * Parity pins: this file is checked against closed forms and identities in
+ * tests/test_oracle_pins.py, never against the HIP path.
+ *
+ * Every input array is fp32 (bf16 inputs arrive as their exact fp32 value);
+ * all arithmetic is double.  Threads split the independent (batch, channel)
+ * pairs; each pair is a strictly sequential loop over t.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <omp.h>
+
+/* log(1 + e^x), evaluated without overflow for large x. */
+static double softplus(double x)
+{
+    if (x > 0.0)
+        return x + log1p(exp(-x));
+    return log1p(exp(x));
+}
+
+static double silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+static double step_delta(double raw, const float *delta_bias, int64_t d, int delta_softplus)
+{
+    double x = raw + (delta_bias ? (double)delta_bias[d] : 0.0);
+    return delta_softplus ? softplus(x) : x;
+}
+
+int oracle_abi_version(void) { return 1; }
+
+/*
+ * u, delta, z: (batch, L, dim); Bm, Cm: (batch, L, N); A: (dim, N);
+ * D_skip, delta_bias: (dim) or NULL; z NULL means no gate;
+ * h0: (batch, dim, N) double or NULL (zeros);
+ * y: (batch, L, dim) double, written; h_last: (batch, dim, N) double or NULL.
+ */
+int oracle_fwd(const float *u, const float *delta, const float *A,
+               const float *Bm, const float *Cm, const float *D_skip,
+               const float *z, const float *delta_bias, int delta_softplus,
+               const double *h0, double *y, double *h_last,
+               int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads)
+{
+    if (batch < 1 || L < 0 || dim < 1 || N < 1)
+        return 1;
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    int64_t pairs = batch * dim;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t p = 0; p < pairs; ++p) {
+                int64_t b = p / dim, d = p % dim;
+                for (int64_t n = 0; n < N; ++n)
+                    h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    int64_t e = (b * L + t) * dim + d;      /* (b, t, d) */
+                    const float *Bt = Bm + (b * L + t) * N;  /* (b, t, :) */
+                    const float *Ct = Cm + (b * L + t) * N;
+                    double dt = step_delta((double)delta[e], delta_bias, d, delta_softplus);
+                    double ut = (double)u[e];
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        double a_bar = exp(dt * (double)A[d * N + n]);
+                        double bu = dt * (double)Bt[n] * ut;
+                        h[n] = a_bar * h[n] + bu;
+                        acc += (double)Ct[n] * h[n];
+                    }
+                    double yv = acc + (D_skip ? (double)D_skip[d] : 0.0) * ut;
+                    if (z)
+                        yv *= silu((double)z[e]);
+                    y[e] = yv;
+                }
+                if (h_last)
+                    for (int64_t n = 0; n < N; ++n)
+                        h_last[(b * dim + d) * N + n] = h[n];
+            }
+            free(h);
+        }
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * One decode step, in place on the state.
+ * state: (batch, dim, N) double; u, delta, z: (batch, dim); Bm, Cm: (batch, N);
+ * y: (batch, dim) double, written.  Same arithmetic as one t of oracle_fwd.
+ */
+int oracle_state_update(double *state, const float *u, const float *delta, const float *A,
+                        const float *Bm, const float *Cm, const float *D_skip,
+                        const float *z, const float *delta_bias, int delta_softplus,
+                        double *y, int64_t batch, int64_t dim, int64_t N, int nthreads)
+{
+    if (batch < 1 || dim < 1 || N < 1)
+        return 1;
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    int64_t pairs = batch * dim;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < pairs; ++p) {
+        int64_t b = p / dim, d = p % dim;
+        double *h = state + p * N;
+        const float *Bt = Bm + b * N;
+        const float *Ct = Cm + b * N;
+        double dt = step_delta((double)delta[p], delta_bias, d, delta_softplus);
+        double ut = (double)u[p];
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double a_bar = exp(dt * (double)A[d * N + n]);
+            h[n] = a_bar * h[n] + dt * (double)Bt[n] * ut;
+            acc += (double)Ct[n] * h[n];
+        }
+        double yv = acc + (D_skip ? (double)D_skip[d] : 0.0) * ut;
+        if (z)
+            yv *= silu((double)z[p]);
+        y[p] = yv;
+    }
+    return 0;
+}
