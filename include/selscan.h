@@ -1,0 +1,165 @@
+/*
+ * selscan.h -- C ABI of the MI355X (gfx950) S6 selective-scan library.
+ *
+ * Two operations, both defined on the Mamba pages:
+ *
+ *  selscan_fwd           the selective-scan forward over a whole sequence:
+ *                        Delta_t = softplus(Delta_raw + bias), A_bar = exp(Delta_t A)
+ *                        with diagonal A, B_bar u = Delta_t B_t u_t, the recurrence
+ *                        h_t = A_bar_t * h_{t-1} + B_bar_t u_t, the readout
+ *                        y_t = C_t . h_t + D u_t and the optional SiLU(z) gate.
+ *                        Sources: Mamba tutorial (pwwt.cn) §2.2 (discretisation,
+ *                        B_bar simplified to Delta B), §3.1 (B, C, Delta depend on
+ *                        the input; softplus on Delta), §3.2 (one fused kernel,
+ *                        parallel scan), §4.2 (the reference loop: h starts at 0,
+ *                        readout after the update, + x D, then * SiLU(z));
+ *                        Gu & Dao deep-reading report (zako-mio.github.io) §2.3,
+ *                        §2.4 (the state h of shape (B,L,D,N) is never written
+ *                        to HBM; only y of shape (B,L,D) is).
+ *
+ *  selscan_state_update  one decode step of the same recurrence on a resident
+ *                        state: constant memory and O(1) work per token, one
+ *                        state per sample.  Sources: Mamba tutorial §5.1 table
+ *                        and §6.3; paper walkthrough (m.lqnn.cn) §3.2, which
+ *                        names the single-token state update.
+ *
+ * Notation: the pages' B (batch) and D (channels) clash with the input matrix
+ * B and the skip vector D, so the ABI calls them `batch` and `dim`, and the
+ * matrices `Bm`, `Cm` and the skip vector `D_skip`.  N is the state size.
+ *
+ * Layout: every array is dense, row-major (C order), no strides:
+ *   u, delta, z, y          (batch, L, dim)     element type = dtype
+ *   Bm, Cm                  (batch, L, N)       element type = dtype
+ *                           (B_t and C_t are shared by all dim channels)
+ *   A                       (dim, N)            fp32 (diagonal A, one row per channel)
+ *   D_skip, delta_bias      (dim)               fp32
+ *   h0, h_last, state       (batch, dim, N)     fp32
+ * For selscan_state_update the L axis is absent: u, delta, z, y are
+ * (batch, dim) and Bm, Cm are (batch, N).
+ *
+ * dtype: SELSCAN_F32 or SELSCAN_BF16.  It applies to u, delta, Bm, Cm, z and y
+ * together.  A, D_skip, delta_bias and the state are always fp32.  All
+ * arithmetic is fp32; y is rounded to bf16 once, to nearest even.
+ *
+ * Pointers are device pointers (hipMalloc'd or equivalent), 16-byte aligned.
+ * `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Ownership: the caller owns every buffer, the workspace included.  The library
+ * keeps no state between calls.  It never allocates, frees or synchronises.
+ * Inputs are only read.  Outputs must not overlap inputs; the exception is
+ * `state`, which selscan_state_update updates in place.  Every buffer must stay
+ * alive until the work queued on `stream` has completed.  Calls on different
+ * streams may run concurrently if each has its own outputs and workspace.
+ *
+ * Errors: every argument check runs on the host, synchronously, BEFORE any
+ * HIP call.  On an argument error the function returns a nonzero status,
+ * queues nothing and touches no output.  SELSCAN_ERR_HIP means a HIP runtime
+ * call (kernel launch) failed; selscan_last_hip_error() then returns the
+ * hipError_t of the calling thread.  Otherwise the calls return SELSCAN_OK as
+ * soon as the work is queued (asynchronous on `stream`).  NaN or Inf in the
+ * inputs propagate to the outputs; there is no trap.
+ */
+#ifndef SELSCAN_H
+#define SELSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SELSCAN_ABI_VERSION 1
+
+enum selscan_dtype {
+    SELSCAN_F32 = 0,
+    SELSCAN_BF16 = 1
+};
+
+enum selscan_status {
+    SELSCAN_OK = 0,
+    SELSCAN_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    SELSCAN_ERR_SHAPE = 2,       /* a size is < 1, or an element count overflows     */
+    SELSCAN_ERR_DTYPE = 3,       /* dtype is neither SELSCAN_F32 nor SELSCAN_BF16    */
+    SELSCAN_ERR_UNSUPPORTED = 4, /* N not in the compiled set, or a pointer that is
+                                    not 16-byte aligned                              */
+    SELSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
+    SELSCAN_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer        */
+    SELSCAN_ERR_HIP = 7          /* a HIP runtime call failed                        */
+};
+
+/* SELSCAN_ABI_VERSION of the built library. */
+int selscan_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *selscan_status_string(int status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int selscan_last_hip_error(void);
+
+/* Nonzero if N is a compiled state size (4, 8, 16, 32 and 64 are built). */
+int selscan_supports_n(int64_t N);
+
+/*
+ * Bytes of device workspace selscan_fwd needs for this shape (0 is possible:
+ * then `workspace` may be NULL).  Returns 0 for invalid arguments too; call
+ * selscan_fwd to get the status.  The workspace holds per-chunk carries of
+ * the sequence split.  Its contents need no initialisation, and its size
+ * depends only on these arguments.
+ */
+size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype);
+
+/*
+ * Selective-scan forward.
+ *
+ *   u          (batch, L, dim)  dtype   input sequence u_t (x in the pages)
+ *   delta      (batch, L, dim)  dtype   Delta_raw, before bias and softplus
+ *   A          (dim, N)         fp32    diagonal state matrix (negative for decay)
+ *   Bm, Cm     (batch, L, N)    dtype   input-dependent B_t and C_t
+ *   D_skip     (dim)            fp32    skip term D; NULL means 0
+ *   z          (batch, L, dim)  dtype   gate input; NULL means no gate
+ *   delta_bias (dim)            fp32    added to Delta_raw; NULL means 0
+ *   delta_softplus  1: Delta_t = softplus(Delta_raw + bias); 0: Delta_raw + bias
+ *   h0         (batch, dim, N)  fp32    initial state; NULL means zeros
+ *   y          (batch, L, dim)  dtype   output, written
+ *   h_last     (batch, dim, N)  fp32    final state h_L, written; NULL to skip
+ *   workspace / workspace_bytes         >= selscan_fwd_workspace_bytes(...)
+ *   stream                              hipStream_t as void*
+ *
+ * Required: batch, L, dim >= 1; N supported; u, delta, A, Bm, Cm, y non-NULL.
+ */
+int selscan_fwd(const void *u, const void *delta, const float *A,
+                const void *Bm, const void *Cm, const float *D_skip,
+                const void *z, const float *delta_bias, int delta_softplus,
+                const float *h0, void *y, float *h_last,
+                int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step, updating `state` in place:
+ *   state[b,d,n] <- exp(Delta A[d,n]) * state[b,d,n] + Delta Bm[b,n] u[b,d]
+ *   y[b,d]        = (sum_n Cm[b,n] state[b,d,n] + D[d] u[b,d]) * SiLU(z[b,d])
+ * with Delta = softplus(delta[b,d] + bias[d]) (or the raw sum), exactly one
+ * t-step of selscan_fwd.
+ *
+ *   state      (batch, dim, N)  fp32    read and written in place
+ *   u, delta   (batch, dim)     dtype
+ *   A          (dim, N)         fp32
+ *   Bm, Cm     (batch, N)       dtype
+ *   D_skip, delta_bias (dim)    fp32    NULL means 0
+ *   z          (batch, dim)     dtype   NULL means no gate
+ *   y          (batch, dim)     dtype   output, written
+ *
+ * Required: batch, dim >= 1; N supported; state, u, delta, A, Bm, Cm, y non-NULL.
+ */
+int selscan_state_update(float *state, const void *u, const void *delta, const float *A,
+                         const void *Bm, const void *Cm, const float *D_skip,
+                         const void *z, const float *delta_bias, int delta_softplus,
+                         void *y, int64_t batch, int64_t dim, int64_t N, int dtype,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELSCAN_H */

@@ -1,0 +1,22 @@
+"""MI355X (gfx950) S6 selective scan: Python binding of libselscan.
+
+The work runs in the HIP kernels behind the C ABI in ``include/selscan.h``.
+This module only marshals torch tensors (device memory) and the current HIP
+stream into that ABI.  Nothing here computes any step of the scan, and there
+is no CPU fallback.  If ``libselscan.so`` is missing, every call raises.
+
+    y = selscan_fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias)
+    y, h_last = selscan_fwd(..., return_last_state=True)
+    y = selscan_state_update(state, u, delta, A, Bm, Cm, D_skip, z, delta_bias)
+"""
+from ._abi import (  # noqa: F401
+    SELSCAN_BF16,
+    SELSCAN_F32,
+    SelscanError,
+    lib,
+    lib_path,
+    selscan_fwd,
+    selscan_fwd_workspace_bytes,
+    selscan_state_update,
+    status_string,
+)

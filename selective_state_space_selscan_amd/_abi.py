@@ -1,0 +1,198 @@
+"""ctypes binding of libselscan (C ABI in include/selscan.h).
+
+Argument marshalling only: dtype and device checks, ``.contiguous()``,
+allocation of outputs and workspace with torch, the current HIP stream, and
+status codes turned into exceptions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+SELSCAN_F32 = 0
+SELSCAN_BF16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libselscan.so")
+_lib = None
+
+
+class SelscanError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        msg = "%s failed: status %d (%s)" % (where, status, status_string(status))
+        if hip_error:
+            msg += ", hipError %d" % hip_error
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libselscan.so with argument types set; raises if not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libselscan.so is not built (%s); run "
+                               "`python -m selective_state_space_selscan_amd.build`" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.selscan_abi_version.restype = I
+        L.selscan_abi_version.argtypes = []
+        L.selscan_status_string.restype = ctypes.c_char_p
+        L.selscan_status_string.argtypes = [I]
+        L.selscan_last_hip_error.restype = I
+        L.selscan_last_hip_error.argtypes = []
+        L.selscan_supports_n.restype = I
+        L.selscan_supports_n.argtypes = [I64]
+        L.selscan_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.selscan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+        L.selscan_fwd.restype = I
+        L.selscan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I,
+                                  P, ctypes.c_size_t, P]
+        L.selscan_state_update.restype = I
+        L.selscan_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().selscan_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SELSCAN_F32
+    if t.dtype == torch.bfloat16:
+        return SELSCAN_BF16
+    raise TypeError("u/delta/Bm/Cm/z must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _prep(t: Optional[torch.Tensor], dtype, device, name: str, shape) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    t = t.contiguous()
+    if t.data_ptr() % 16:
+        t = t.clone()
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def selscan_fwd_workspace_bytes(batch: int, L: int, dim: int, N: int, dtype: int) -> int:
+    return int(lib().selscan_fwd_workspace_bytes(batch, L, dim, N, dtype))
+
+
+def selscan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                Cm: torch.Tensor, D_skip: Optional[torch.Tensor] = None,
+                z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                return_last_state: bool = False, y: Optional[torch.Tensor] = None,
+                h_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None):
+    """Selective-scan forward through ``selscan_fwd`` (asynchronous on the stream).
+
+    u, delta, z: (batch, L, dim); Bm, Cm: (batch, L, N) in float32 or bfloat16;
+    A: (dim, N), D_skip, delta_bias: (dim,), h0: (batch, dim, N) in float32.
+    Returns y, or (y, h_last) when ``return_last_state``."""
+    L_ = lib()
+    dev = u.device
+    dt = u.dtype
+    code = _dtype_code(u)
+    batch, L, dim = u.shape
+    N = A.shape[-1]
+    u = _prep(u, dt, dev, "u", (batch, L, dim))
+    delta = _prep(delta, dt, dev, "delta", (batch, L, dim))
+    Bm = _prep(Bm, dt, dev, "Bm", (batch, L, N))
+    Cm = _prep(Cm, dt, dev, "Cm", (batch, L, N))
+    z = _prep(z, dt, dev, "z", (batch, L, dim))
+    A = _prep(A, torch.float32, dev, "A", (dim, N))
+    D_skip = _prep(D_skip, torch.float32, dev, "D_skip", (dim,))
+    delta_bias = _prep(delta_bias, torch.float32, dev, "delta_bias", (dim,))
+    h0 = _prep(h0, torch.float32, dev, "h0", (batch, dim, N))
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    else:
+        y = _check_out(y, dt, dev, "y", (batch, L, dim))
+    if return_last_state and h_last is None:
+        h_last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    elif h_last is not None:
+        h_last = _check_out(h_last, torch.float32, dev, "h_last", (batch, dim, N))
+    ws_bytes = int(L_.selscan_fwd_workspace_bytes(batch, L, dim, N, code))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = L_.selscan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
+                        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(y),
+                        _ptr(h_last), batch, L, dim, N, code,
+                        _ptr(workspace) if ws_bytes else None,
+                        workspace.numel() * workspace.element_size() if ws_bytes else 0,
+                        _stream(dev, stream))
+    if rc != 0:
+        raise SelscanError(rc, "selscan_fwd", L_.selscan_last_hip_error())
+    return (y, h_last) if return_last_state else y
+
+
+def selscan_state_update(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor,
+                         A: torch.Tensor, Bm: torch.Tensor, Cm: torch.Tensor,
+                         D_skip: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                         delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
+                         y: Optional[torch.Tensor] = None,
+                         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One decode step through ``selscan_state_update``; ``state`` (batch, dim, N)
+    float32 is updated in place.  u, delta, z: (batch, dim); Bm, Cm: (batch, N)."""
+    L_ = lib()
+    dev = u.device
+    dt = u.dtype
+    code = _dtype_code(u)
+    batch, dim = u.shape
+    N = A.shape[-1]
+    state = _check_out(state, torch.float32, dev, "state", (batch, dim, N))
+    u = _prep(u, dt, dev, "u", (batch, dim))
+    delta = _prep(delta, dt, dev, "delta", (batch, dim))
+    Bm = _prep(Bm, dt, dev, "Bm", (batch, N))
+    Cm = _prep(Cm, dt, dev, "Cm", (batch, N))
+    z = _prep(z, dt, dev, "z", (batch, dim))
+    A = _prep(A, torch.float32, dev, "A", (dim, N))
+    D_skip = _prep(D_skip, torch.float32, dev, "D_skip", (dim,))
+    delta_bias = _prep(delta_bias, torch.float32, dev, "delta_bias", (dim,))
+    if y is None:
+        y = torch.empty((batch, dim), dtype=dt, device=dev)
+    else:
+        y = _check_out(y, dt, dev, "y", (batch, dim))
+    rc = L_.selscan_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                 _ptr(D_skip), _ptr(z), _ptr(delta_bias),
+                                 int(bool(delta_softplus)), _ptr(y), batch, dim, N, code,
+                                 _stream(dev, stream))
+    if rc != 0:
+        raise SelscanError(rc, "selscan_state_update", L_.selscan_last_hip_error())
+    return y
+
+
+def _check_out(t: torch.Tensor, dtype, device, name: str, shape) -> torch.Tensor:
+    """Outputs are written in place, so they must already be dense and aligned."""
+    if t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be %s %s on %s" % (name, dtype, tuple(shape), device))
+    if not t.is_contiguous() or t.data_ptr() % 16:
+        raise ValueError("%s must be contiguous and 16-byte aligned" % name)
+    return t

@@ -1,0 +1,178 @@
+// C-ABI layer of libselscan: host-side argument checks, launch planning and
+// status codes.  The contract is documented in include/selscan.h.
+//
+// Every check below runs before the first HIP call, so an invalid call
+// queues nothing and leaves outputs untouched (and works on a host without
+// a GPU, which the CPU test suite relies on).
+#include "../../include/selscan.h"
+#include "kernels.hpp"
+
+#include <stdint.h>
+#include <string.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool supported_n(int64_t N)
+{
+    return N == 4 || N == 8 || N == 16 || N == 32 || N == 64;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// a * b * c without overflow past 2^62; returns -1 on overflow.
+int64_t checked_count(int64_t a, int64_t b, int64_t c)
+{
+    const int64_t lim = (int64_t)1 << 62;
+    if (a <= 0 || b <= 0 || c <= 0)
+        return -1;
+    if (a > lim / b)
+        return -1;
+    int64_t ab = a * b;
+    if (ab > lim / c)
+        return -1;
+    return ab * c;
+}
+
+struct Range {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlaps(Range a, Range b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0)
+        return false;
+    uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + (uintptr_t)a.bytes;
+    uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + (uintptr_t)b.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+int finish_launch(hipError_t e)
+{
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return SELSCAN_ERR_HIP;
+    }
+    return SELSCAN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int selscan_abi_version(void) { return SELSCAN_ABI_VERSION; }
+
+const char *selscan_status_string(int status)
+{
+    switch (status) {
+    case SELSCAN_OK: return "ok";
+    case SELSCAN_ERR_NULL: return "a required pointer is NULL";
+    case SELSCAN_ERR_SHAPE: return "a size is < 1 or an element count overflows";
+    case SELSCAN_ERR_DTYPE: return "dtype is not SELSCAN_F32 or SELSCAN_BF16";
+    case SELSCAN_ERR_UNSUPPORTED: return "unsupported N or a pointer not 16-byte aligned";
+    case SELSCAN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SELSCAN_ERR_ALIAS: return "an output overlaps an input";
+    case SELSCAN_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+    }
+}
+
+int selscan_last_hip_error(void) { return g_last_hip_error; }
+
+int selscan_supports_n(int64_t N) { return supported_n(N) ? 1 : 0; }
+
+size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype)
+{
+    (void)batch; (void)L; (void)dim; (void)N; (void)dtype;
+    return 0;
+}
+
+int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+                const float *D_skip, const void *z, const float *delta_bias, int delta_softplus,
+                const float *h0, void *y, float *h_last, int64_t batch, int64_t L, int64_t dim,
+                int64_t N, int dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
+        return SELSCAN_ERR_DTYPE;
+    const int64_t elems = checked_count(batch, L, dim);
+    const int64_t bcn = checked_count(batch, L, N > 0 ? N : 1);
+    const int64_t states = checked_count(batch, dim, N > 0 ? N : 1);
+    if (elems < 0 || bcn < 0 || states < 0 || N < 1)
+        return SELSCAN_ERR_SHAPE;
+    if (!u || !delta || !A || !Bm || !Cm || !y)
+        return SELSCAN_ERR_NULL;
+    if (!supported_n(N))
+        return SELSCAN_ERR_UNSUPPORTED;
+    const void *all[] = {u, delta, A, Bm, Cm, D_skip, z, delta_bias, h0, y, h_last, workspace};
+    for (const void *p : all)
+        if (p && !aligned16(p))
+            return SELSCAN_ERR_UNSUPPORTED;
+    const size_t need = selscan_fwd_workspace_bytes(batch, L, dim, N, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return SELSCAN_ERR_WORKSPACE;
+
+    const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
+    const Range ins[] = {{u, elems * es},     {delta, elems * es},     {A, dim * N * 4},
+                         {Bm, bcn * es},      {Cm, bcn * es},          {D_skip, dim * 4},
+                         {z, elems * es},     {delta_bias, dim * 4},   {h0, states * 4},
+                         {workspace, (int64_t)need}};
+    const Range outs[] = {{y, elems * es}, {h_last, states * 4}};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return SELSCAN_ERR_ALIAS;
+    if (overlaps(outs[0], outs[1]))
+        return SELSCAN_ERR_ALIAS;
+
+    selscan::FwdArgs a;
+    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
+    a.delta_bias = delta_bias; a.delta_softplus = delta_softplus ? 1 : 0; a.h0 = h0; a.y = y;
+    a.h_last = h_last; a.batch = batch; a.L = L; a.dim = dim; a.N = N; a.dtype = dtype;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
+}
+
+int selscan_state_update(float *state, const void *u, const void *delta, const float *A,
+                         const void *Bm, const void *Cm, const float *D_skip, const void *z,
+                         const float *delta_bias, int delta_softplus, void *y, int64_t batch,
+                         int64_t dim, int64_t N, int dtype, void *stream)
+{
+    if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
+        return SELSCAN_ERR_DTYPE;
+    const int64_t elems = checked_count(batch, dim, 1);
+    const int64_t states = checked_count(batch, dim, N > 0 ? N : 1);
+    const int64_t bcn = checked_count(batch, N > 0 ? N : 1, 1);
+    if (elems < 0 || states < 0 || bcn < 0 || N < 1)
+        return SELSCAN_ERR_SHAPE;
+    if (!state || !u || !delta || !A || !Bm || !Cm || !y)
+        return SELSCAN_ERR_NULL;
+    if (!supported_n(N))
+        return SELSCAN_ERR_UNSUPPORTED;
+    const void *all[] = {state, u, delta, A, Bm, Cm, D_skip, z, delta_bias, y};
+    for (const void *p : all)
+        if (p && !aligned16(p))
+            return SELSCAN_ERR_UNSUPPORTED;
+
+    const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
+    const Range ins[] = {{u, elems * es},  {delta, elems * es}, {A, dim * N * 4},
+                         {Bm, bcn * es},   {Cm, bcn * es},      {D_skip, dim * 4},
+                         {z, elems * es},  {delta_bias, dim * 4}};
+    const Range st = {state, states * 4};
+    const Range yo = {y, elems * es};
+    for (const Range &i : ins)
+        if (overlaps(st, i) || overlaps(yo, i))
+            return SELSCAN_ERR_ALIAS;
+    if (overlaps(st, yo))
+        return SELSCAN_ERR_ALIAS;
+
+    selscan::StepArgs a;
+    a.state = state; a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
+    a.D_skip = D_skip; a.z = z; a.delta_bias = delta_bias;
+    a.delta_softplus = delta_softplus ? 1 : 0; a.y = y; a.batch = batch; a.dim = dim; a.N = N;
+    a.dtype = dtype;
+    return finish_launch(selscan::launch_state_update(a, (hipStream_t)stream));
+}
+
+} // extern "C"

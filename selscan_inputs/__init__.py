@@ -66,8 +66,8 @@ WORKLOADS = {
 }
 
 
-def bf16_round(x: np.ndarray):
-    """Round fp32 to bf16 (round to nearest, ties to even).
+def bf16_round_np(x: np.ndarray):
+    """Round fp32 to bf16 (round to nearest, ties to even), in numpy.
 
     Returns (bits, widened): ``bits`` is the uint16 bf16 pattern, ``widened``
     the exact fp32 value of that bf16 number.  Inputs are finite draws."""
@@ -76,6 +76,16 @@ def bf16_round(x: np.ndarray):
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     bits = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
     widened = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return bits, widened
+
+
+def bf16_round(x: np.ndarray):
+    """Same result as ``bf16_round_np`` (checked in the tests), through torch's
+    multi-threaded CPU conversion, which is much faster on large draws."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    widened = t.to(torch.float32).numpy()
     return bits, widened
 
 
@@ -184,3 +194,53 @@ def decode_step_inputs(w: Workload, k: int, batch: Optional[int] = None) -> Step
     z = rng.standard_normal((b, w.dim), dtype=np.float32) if w.gate else None
     return StepInputs(_store(u, w.dtype), _store(delta, w.dtype), _store(Bm, w.dtype),
                       _store(Cm, w.dtype), _store(z, w.dtype) if w.gate else None)
+
+
+def to_torch(t: Optional[Tensor], dtype: str, device):
+    """Upload one input array in its storage dtype (bf16 bits or fp32)."""
+    import torch
+    if t is None:
+        return None
+    if dtype == BF16:
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(t.value).to(device)
+
+
+def fwd_tensors(inp: FwdInputs, device) -> dict:
+    """The forward inputs as device tensors, keyed like the ABI arguments."""
+    import torch
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return dict(u=to_torch(inp.u, inp.dtype, device), delta=to_torch(inp.delta, inp.dtype, device),
+                A=f(inp.A), Bm=to_torch(inp.Bm, inp.dtype, device),
+                Cm=to_torch(inp.Cm, inp.dtype, device), D_skip=f(inp.D_skip),
+                z=to_torch(inp.z, inp.dtype, device), delta_bias=f(inp.delta_bias), h0=f(inp.h0))
+
+
+def step_tensors(st: StepInputs, dtype: str, device) -> dict:
+    return dict(u=to_torch(st.u, dtype, device), delta=to_torch(st.delta, dtype, device),
+                Bm=to_torch(st.Bm, dtype, device), Cm=to_torch(st.Cm, dtype, device),
+                z=to_torch(st.z, dtype, device))
+
+
+def channel_slice(inp: FwdInputs, channels: np.ndarray) -> FwdInputs:
+    """The inputs restricted to a subset of channels.  Channels are independent
+    in the scan, so the oracle on the slice gives those channels' outputs."""
+    c = np.asarray(channels)
+    sl = lambda t: None if t is None else Tensor(np.ascontiguousarray(t.value[..., c]),
+                                                 None if t.bits is None else
+                                                 np.ascontiguousarray(t.bits[..., c]))
+    return FwdInputs(dtype=inp.dtype, batch=inp.batch, L=inp.L, dim=len(c), N=inp.N,
+                     u=sl(inp.u), delta=sl(inp.delta), Bm=inp.Bm, Cm=inp.Cm, z=sl(inp.z),
+                     A=np.ascontiguousarray(inp.A[c]),
+                     D_skip=None if inp.D_skip is None else np.ascontiguousarray(inp.D_skip[c]),
+                     delta_bias=None if inp.delta_bias is None else
+                     np.ascontiguousarray(inp.delta_bias[c]),
+                     h0=None if inp.h0 is None else np.ascontiguousarray(inp.h0[:, c]))
+
+
+def decode_block(w: Workload, k0: int, k1: int, threads: int = 8):
+    """Inputs of decode steps k0..k1-1, drawn in parallel (each step has its own
+    seeded generator, so the result does not depend on ``threads``)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        return list(ex.map(lambda k: decode_step_inputs(w, k), range(k0, k1)))

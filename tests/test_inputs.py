@@ -10,10 +10,12 @@ def test_bf16_round_matches_torch_rne():
     x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
                         np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0, -0.0,
                                   1e-30, 3e38], np.float32)])
-    bits, wide = si.bf16_round(x)
+    bits, wide = si.bf16_round_np(x)
     t = torch.from_numpy(x).to(torch.bfloat16)
     assert np.array_equal(bits, t.view(torch.int16).numpy().view(np.uint16))
     assert np.array_equal(wide, t.to(torch.float32).numpy())
+    bits2, wide2 = si.bf16_round(x)
+    assert np.array_equal(bits, bits2) and np.array_equal(wide, wide2)
 
 
 def test_generators_are_deterministic():

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every workload and edge case compares the kernel output element by element
+with the oracle on the same seeded inputs.  The large workloads use a sample
+of channels on the oracle side: channels are independent in the scan, so the
+oracle run on the sliced inputs yields exactly those channels' outputs.
+
+Because D*u dominates y (the scan part is a small fraction of it), every
+workload is also run with D_skip = 0 and no gate, and its final state h_L is
+compared too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selscan_inputs as si
+import selective_state_space_selscan_amd as ss
+from parity_util import TOL, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_fwd(inp, device, return_last=True):
+    t = si.fwd_tensors(inp, device)
+    out = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                         t["delta_bias"], True, t["h0"], return_last_state=return_last)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_fwd(inp, device, channels=None, tol=None, what=""):
+    tol = TOL[inp.dtype] if tol is None else tol
+    say("case", what, inp.batch, inp.L, inp.dim, inp.N, inp.dtype)
+    y, hL = run_fwd(inp, device)
+    if channels is None:
+        ey, ehL = oracle.fwd_inputs(inp)
+        gy, ghL = to_np(y), to_np(hL)
+    else:
+        ey, ehL = oracle.fwd_inputs(si.channel_slice(inp, channels))
+        gy, ghL = to_np(y)[..., channels], to_np(hL)[:, channels]
+    ey_ = rel_err(gy, ey)
+    eh_ = rel_err(ghL, ehL)
+    say("  rel_err y=%.3g h_last=%.3g (tol %.1g)" % (ey_, eh_, tol))
+    assert ey_ <= tol, "y rel err %.3g > %.3g" % (ey_, tol)
+    assert eh_ <= tol, "h_last rel err %.3g > %.3g" % (eh_, tol)
+    return y, hL
+
+
+def sample_channels(dim, k, seed=0):
+    rng = np.random.default_rng(seed)
+    c = rng.choice(dim, size=min(k, dim), replace=False)
+    c[:2] = [0, dim - 1]
+    return np.sort(np.unique(c))
+
+
+WORKLOAD_SAMPLES = {"tiny_f32": None, "mamba130m_layer": None, "long_seq": 48,
+                    "large_layer": 96}
+
+
+@pytest.mark.parametrize("name", list(WORKLOAD_SAMPLES))
+@pytest.mark.parametrize("variant", ["as_specified", "scan_only"])
+def test_workload_parity(device, name, variant):
+    w = si.WORKLOADS[name]
+    kw = {} if variant == "as_specified" else dict(D_value=0.0, gate=False)
+    inp = si.workload_fwd_inputs(w, **kw)
+    k = WORKLOAD_SAMPLES[name]
+    ch = None if k is None else sample_channels(w.dim, k)
+    check_fwd(inp, device, ch, what=name + "/" + variant)
+
+
+def test_decode_workload(device):
+    """1024 single-token steps on the resident fp32 state (batch 256, D 5120,
+    N 16), checked against the oracle's recurrence every 64 steps on a sample
+    of channels (all batch rows)."""
+    w = si.WORKLOADS["decode"]
+    A, D, bias = si.decode_params(w)
+    ch = sample_channels(w.dim, 48, seed=1)
+    tA, tD, tb = (torch.from_numpy(x).to(device) for x in (A, D, bias))
+    state = torch.zeros((w.batch, w.dim, w.N), dtype=torch.float32, device=device)
+    ostate = np.zeros((w.batch, len(ch), w.N), dtype=np.float64)
+    worst_y = worst_s = 0.0
+    for k0 in range(0, w.decode_steps, w.check_every):
+        say("decode steps", k0, k0 + w.check_every)
+        block = si.decode_block(w, k0, k0 + w.check_every)
+        for st in block:
+            t = si.step_tensors(st, w.dtype, device)
+            y = ss.selscan_state_update(state, t["u"], t["delta"], tA, t["Bm"], t["Cm"], tD,
+                                        t["z"], tb, True)
+            ey = oracle.state_update(ostate, st.u.value[:, ch], st.delta.value[:, ch], A[ch],
+                                     st.Bm.value, st.Cm.value, D[ch], st.z.value[:, ch],
+                                     bias[ch], True)
+        torch.cuda.synchronize()
+        ry = rel_err(to_np(y)[:, ch], ey)
+        rs = rel_err(to_np(state)[:, ch], ostate)
+        worst_y, worst_s = max(worst_y, ry), max(worst_s, rs)
+        assert ry <= TOL["bf16"] and rs <= TOL["bf16"], (k0, ry, rs)
+    say("  decode worst rel_err y=%.3g state=%.3g" % (worst_y, worst_s))
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+@pytest.mark.parametrize("N", [4, 8, 16, 32, 64])
+def test_every_state_size(device, N, dtype):
+    inp = si.make_fwd_inputs(2, 300, 96, N, dtype, True, seed=100 + N, h0=True, D_value=None)
+    check_fwd(inp, device, what="N%d" % N)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64), (1, 1, 1), (3, 1, 100), (2, 7, 65), (1, 1000, 130),
+                                   (2, 2049, 64), (1, 4097, 192), (5, 129, 33)])
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+def test_ragged_shapes(device, shape, dtype):
+    batch, L, dim = shape
+    inp = si.make_fwd_inputs(batch, L, dim, 16, dtype, True, seed=sum(shape), h0=True)
+    check_fwd(inp, device, what="ragged%s" % (shape,))
+
+
+def test_long_sequence_ragged_with_h0(device):
+    inp = si.make_fwd_inputs(1, 40000, 128, 16, si.BF16, False, seed=7, h0=True, D_value=0.0)
+    check_fwd(inp, device, what="long ragged h0")
+
+
+@pytest.mark.parametrize("softplus_on,bias_on,d_on", [(True, False, True), (False, True, False),
+                                                      (False, False, True)])
+def test_optional_arguments(device, softplus_on, bias_on, d_on):
+    inp = si.make_fwd_inputs(2, 200, 64, 16, si.F32, False, seed=9, with_bias=bias_on,
+                             D_value=1.0 if d_on else None)
+    if not d_on:
+        inp.D_skip = None
+    if not softplus_on:
+        # raw Delta must stay positive: use |Delta_raw| * 0.1
+        inp.delta = si.Tensor(np.abs(inp.delta.value) * np.float32(0.1))
+        if inp.delta_bias is not None:
+            inp.delta_bias = np.abs(inp.delta_bias) * np.float32(0.01)
+    t = si.fwd_tensors(inp, device)
+    y, hL = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], None,
+                           t["delta_bias"], softplus_on, None, return_last_state=True)
+    ey, ehL = oracle.fwd(inp.u.value, inp.delta.value, inp.A, inp.Bm.value, inp.Cm.value,
+                         inp.D_skip, None, inp.delta_bias, softplus_on)
+    assert rel_err(to_np(y), ey) <= TOL["f32"]
+    assert rel_err(to_np(hL), ehL) <= TOL["f32"]
+
+
+def test_softplus_accuracy_through_abi(device):
+    """L = 1, u = B = 1, no h0: h_last = Delta = softplus(x).  Sweeps x over the
+    range the workloads reach (and beyond), elementwise relative error."""
+    x = np.concatenate([np.linspace(-30, 30, 2048), np.linspace(-10, -2, 2048)]).astype(np.float32)
+    dim = x.size
+    dev = device
+    one = torch.ones((1, 1, dim), device=dev)
+    zero = torch.zeros((1, 1, dim), device=dev)
+    A = -torch.ones((dim, 4), device=dev)
+    B1 = torch.ones((1, 1, 4), device=dev)
+    bias = torch.from_numpy(x).to(dev)
+    _, hL = ss.selscan_fwd(one, zero, A, B1, B1, None, None, bias, True, None,
+                           return_last_state=True)
+    got = to_np(hL)[0, :, 0]
+    want = np.logaddexp(0.0, x.astype(np.float64))
+    err = np.max(np.abs(got - want) / want)
+    say("softplus max rel err %.3g" % err)
+    assert err < 2e-6
+
+
+def test_delta_limits_on_gpu(device):
+    inp = si.make_fwd_inputs(2, 64, 128, 16, si.F32, True, seed=11, h0=True)
+    inp.delta = si.Tensor(np.full_like(inp.delta.value, -40.0))
+    inp.delta_bias = None
+    y, hL = run_fwd(inp, device)
+    assert rel_err(to_np(hL), inp.h0) < 1e-5
+    ey, _ = oracle.fwd_inputs(inp)
+    assert rel_err(to_np(y), ey) <= TOL["f32"]
+
+
+def test_bitwise_repeatable(device):
+    inp = si.workload_fwd_inputs(si.WORKLOADS["mamba130m_layer"], L=512)
+    outs = [run_fwd(inp, device) for _ in range(3)]
+    for y, h in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(h, outs[0][1])
+
+
+@pytest.mark.parametrize("L1", [1, 100, 1024, 1500])
+def test_split_invariance_on_gpu(device, L1):
+    inp = si.make_fwd_inputs(2, 3000, 128, 16, si.F32, True, seed=13, h0=True)
+    t = si.fwd_tensors(inp, device)
+    y, hL = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                           t["delta_bias"], True, t["h0"], return_last_state=True)
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    ya, ha = ss.selscan_fwd(sl(t["u"], 0, L1), sl(t["delta"], 0, L1), t["A"], sl(t["Bm"], 0, L1),
+                            sl(t["Cm"], 0, L1), t["D_skip"], sl(t["z"], 0, L1), t["delta_bias"],
+                            True, t["h0"], return_last_state=True)
+    yb, hb = ss.selscan_fwd(sl(t["u"], L1, None), sl(t["delta"], L1, None), t["A"],
+                            sl(t["Bm"], L1, None), sl(t["Cm"], L1, None), t["D_skip"],
+                            sl(t["z"], L1, None), t["delta_bias"], True, ha,
+                            return_last_state=True)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(torch.cat([ya, yb], 1)), to_np(y)) <= TOL["f32"]
+    assert rel_err(to_np(hb), to_np(hL)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+def test_state_update_matches_forward(device, dtype):
+    """L decode steps from h0 give the forward's y_t and h_L."""
+    batch, L, dim, N = 3, 24, 160, 16
+    inp = si.make_fwd_inputs(batch, L, dim, N, dtype, True, seed=17, h0=True)
+    t = si.fwd_tensors(inp, device)
+    y, hL = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                           t["delta_bias"], True, t["h0"], return_last_state=True)
+    state = t["h0"].clone()
+    ys = []
+    for s in range(L):
+        ys.append(ss.selscan_state_update(state, t["u"][:, s].contiguous(),
+                                          t["delta"][:, s].contiguous(), t["A"],
+                                          t["Bm"][:, s].contiguous(), t["Cm"][:, s].contiguous(),
+                                          t["D_skip"], t["z"][:, s].contiguous(),
+                                          t["delta_bias"], True))
+    torch.cuda.synchronize()
+    ey, ehL = oracle.fwd_inputs(inp)
+    assert rel_err(to_np(torch.stack(ys, 1)), ey) <= TOL[dtype]
+    assert rel_err(to_np(state), ehL) <= TOL[dtype]
+    assert rel_err(to_np(state), to_np(hL)) <= TOL[dtype]
+
+
+def test_state_update_ragged_and_small_n(device):
+    for batch, dim, N in [(1, 1, 4), (3, 100, 8), (2, 257, 32), (1, 64, 64)]:
+        rng = np.random.default_rng(batch * 1000 + dim + N)
+        f = lambda *s: rng.standard_normal(s).astype(np.float32)
+        st = f(batch, dim, N)
+        u, dl, z, Bv, Cv = f(batch, dim), 0.5 * f(batch, dim), f(batch, dim), f(batch, N), f(batch, N)
+        A = si.s4d_real_A(dim, N)
+        D = f(dim)
+        bias = si.dt_bias(rng, dim)
+        T = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        gs = T(st)
+        y = ss.selscan_state_update(gs, T(u), T(dl), T(A), T(Bv), T(Cv), T(D), T(z), T(bias), True)
+        os_ = st.astype(np.float64)
+        ey = oracle.state_update(os_, u, dl, A, Bv, Cv, D, z, bias, True)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(y), ey) <= TOL["f32"]
+        assert rel_err(to_np(gs), os_) <= TOL["f32"]
