@@ -46,6 +46,10 @@ struct StepArgs {
 // Serial forward: one lane per (batch, channel), whole sequence in-lane.
 hipError_t launch_fwd_serial(const FwdArgs &a, hipStream_t stream);
 
+// Chunked forward (the fast path): workspace bytes it needs, and the launch.
+size_t fwd_chunked_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+hipError_t launch_fwd_chunked(const FwdArgs &a, hipStream_t stream);
+
 // Decode step.
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);
 

@@ -8,6 +8,7 @@
 #include "kernels.hpp"
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 namespace {
@@ -20,6 +21,14 @@ bool supported_n(int64_t N)
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// SELSCAN_FORCE_PLAN=serial routes the forward through the serial kernel (one
+// lane per (batch, channel)); it exists for ablations.  Default: chunked.
+bool force_serial()
+{
+    const char *e = getenv("SELSCAN_FORCE_PLAN");
+    return e && strcmp(e, "serial") == 0;
+}
 
 // a * b * c without overflow past 2^62; returns -1 on overflow.
 int64_t checked_count(int64_t a, int64_t b, int64_t c)
@@ -85,8 +94,10 @@ int selscan_supports_n(int64_t N) { return supported_n(N) ? 1 : 0; }
 
 size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype)
 {
-    (void)batch; (void)L; (void)dim; (void)N; (void)dtype;
-    return 0;
+    if ((dtype != SELSCAN_F32 && dtype != SELSCAN_BF16) || !supported_n(N) ||
+        checked_count(batch, L, dim) < 0 || checked_count(batch, L, N) < 0)
+        return 0;
+    return selscan::fwd_chunked_workspace_bytes(batch, L, dim, N);
 }
 
 int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
@@ -131,7 +142,9 @@ int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm
     a.delta_bias = delta_bias; a.delta_softplus = delta_softplus ? 1 : 0; a.h0 = h0; a.y = y;
     a.h_last = h_last; a.batch = batch; a.L = L; a.dim = dim; a.N = N; a.dtype = dtype;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
+    if (force_serial())
+        return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
+    return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
 }
 
 int selscan_state_update(float *state, const void *u, const void *delta, const float *A,
