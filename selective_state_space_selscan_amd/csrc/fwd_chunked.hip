@@ -40,6 +40,7 @@
 // part but the last, the part's aggregate (sum Delta, end state from zero) into
 // the workspace; the main pass folds the aggregates of the parts before its own
 // into its initial carry.
+#include "buffer_io.hpp"
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -71,45 +72,6 @@ __global__ __launch_bounds__(256) void bc_transpose_kernel(
         BT[dst] = valid ? load_elem(Bm, src) : 0.0f;
         CT[dst] = valid ? load_elem(Cm, src) : 0.0f;
     }
-}
-
-// Raw buffer access (MUBUF) with a per-segment descriptor: the base address
-// and byte range are scalar, the per-lane offset is lane * sizeof(element), and
-// the per-timestep offset is a scalar, so no VALU goes into addressing.  Loads
-// past the range return 0 and stores past it are dropped, which covers the
-// ragged end of the sequence.  Word 3 = 0x00020000 is the gfx9-family raw
-// buffer format (32-bit data format).
-constexpr int kBufWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    const int nrec = bytes > 0 ? (int)bytes : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nrec, kBufWord3);
-}
-__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float *)
-{
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, const uint16_t *)
-{
-    return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-}
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v, float *)
-{
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
-}
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v, uint16_t *)
-{
-    // v_cvt_pk_bf16_f32: round to nearest even, NaN preserved
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, voff, soff, 0);
-}
-
-// B^T / C^T columns are read through the constant address space so that the
-// wave-uniform reads become scalar loads (s_load_dwordx16) into SGPRs.
-typedef __attribute__((address_space(4))) const float const_f32;
-__device__ __forceinline__ const const_f32 *as_const(const float *p)
-{
-    return (const const_f32 *)(uintptr_t)p;
 }
 
 // Phase A of one chunk for one wave: per-timestep quantities of the wave's

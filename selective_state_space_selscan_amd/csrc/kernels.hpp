@@ -50,6 +50,11 @@ hipError_t launch_fwd_serial(const FwdArgs &a, hipStream_t stream);
 size_t fwd_chunked_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_chunked(const FwdArgs &a, hipStream_t stream);
 
+// Streaming forward (default): independent waves over sequence parts, with a
+// summary pre-pass when the sequence is split.
+size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
+
 // Decode step.
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);
 

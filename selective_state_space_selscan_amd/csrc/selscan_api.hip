@@ -22,12 +22,19 @@ bool supported_n(int64_t N)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// SELSCAN_FORCE_PLAN=serial routes the forward through the serial kernel (one
-// lane per (batch, channel)); it exists for ablations.  Default: chunked.
-bool force_serial()
+// Forward plans.  Default: the streaming kernel.  SELSCAN_FORCE_PLAN=chunked
+// or =serial selects the workgroup-chunked or the one-lane-per-channel kernel
+// (ablations; all three compute the same recurrence).
+enum Plan { PLAN_STREAM, PLAN_CHUNKED, PLAN_SERIAL };
+
+Plan forced_plan()
 {
     const char *e = getenv("SELSCAN_FORCE_PLAN");
-    return e && strcmp(e, "serial") == 0;
+    if (e && strcmp(e, "serial") == 0)
+        return PLAN_SERIAL;
+    if (e && strcmp(e, "chunked") == 0)
+        return PLAN_CHUNKED;
+    return PLAN_STREAM;
 }
 
 // a * b * c without overflow past 2^62; returns -1 on overflow.
@@ -97,7 +104,9 @@ size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_
     if ((dtype != SELSCAN_F32 && dtype != SELSCAN_BF16) || !supported_n(N) ||
         checked_count(batch, L, dim) < 0 || checked_count(batch, L, N) < 0)
         return 0;
-    return selscan::fwd_chunked_workspace_bytes(batch, L, dim, N);
+    const size_t a = selscan::fwd_chunked_workspace_bytes(batch, L, dim, N);
+    const size_t b = selscan::fwd_stream_workspace_bytes(batch, L, dim, N);
+    return a > b ? a : b;
 }
 
 int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
@@ -142,9 +151,14 @@ int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm
     a.delta_bias = delta_bias; a.delta_softplus = delta_softplus ? 1 : 0; a.h0 = h0; a.y = y;
     a.h_last = h_last; a.batch = batch; a.L = L; a.dim = dim; a.N = N; a.dtype = dtype;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    if (force_serial())
+    switch (forced_plan()) {
+    case PLAN_SERIAL:
         return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
-    return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
+    case PLAN_CHUNKED:
+        return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
+    default:
+        return finish_launch(selscan::launch_fwd_stream(a, (hipStream_t)stream));
+    }
 }
 
 int selscan_state_update(float *state, const void *u, const void *delta, const float *A,
