@@ -1,21 +1,34 @@
 """Throughput of the S6 selective-scan forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --pmc-run            # workload for rocprofv3 --pmc (see below)
+    python bench.py --parse-pmc FETCH_DIR WRITE_DIR   # -> profiles/traffic_<workload>.json
 
-One step = one selscan_fwd pass over one batch of the workload (default: one
-Mamba-130M layer, batch 8, L 2048, D 1536, N 16, bf16 inputs, fp32 state,
-SiLU(z) gate).  Inputs are seeded synthetic data, resident in HBM before the
-timed region.  Several copies of the input set rotate between steps so that
-consecutive steps do not find their inputs in the 256 MB last-level cache.
+One step = one selscan_fwd call over one batch of the workload.  The default
+workload is one Mamba-130M layer: batch 8, L 2048, D 1536, N 16, bf16 inputs,
+fp32 state, SiLU(z) gate.  Inputs are seeded synthetic data, resident in HBM
+before the timed region.  Several copies of the input set rotate between
+steps so that consecutive steps do not find their inputs in the 256 MB
+last-level cache.
 
-Prints one JSON line: elements (batch*L*dim) per second as ``value``, HBM GB/s
-from the algorithmic bytes, the roofline entry of the scan kernel (average
-launch time measured with HIP events on the launch stream), and the CPU
-oracle timed on a bounded sample of the same workload on the host cores.
+The JSON line carries:
+  value      elements (batch*L*dim) per second over the timed steps;
+  roofline   the forward call (summary pass + main pass) against the VALU
+             roofline: the path is bound by fp32 vector arithmetic, not by HBM
+             (see algorithmic_valu_slots).  The call's average duration comes
+             from HIP events recorded on the launch stream around each call;
+  traffic    HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+             scaled by the same counters on a plain 1 GiB copy, read from
+             profiles/traffic_<workload>.json if the kernel sources are
+             unchanged since it was taken, else null;
+  hbm_*      algorithmic bytes per call / step time, against the 8 TB/s peak;
+  cpu_baseline  the CPU oracle (fp64, OpenMP) on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +40,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# fp32 vector issue rate without packed instructions: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz = 39.3e12 lane-operations per second (one FMA = one slot).
+VALU_PEAK_SLOTS = 256 * 4 * 16 * 2.4e9
+COPY_CAL_BYTES = 1 << 30
 
 
 def algorithmic_bytes(batch, L, dim, N, es, gate, with_last=False, with_h0=False):
@@ -43,68 +60,176 @@ def algorithmic_bytes(batch, L, dim, N, es, gate, with_last=False, with_h0=False
     return b
 
 
-def cpu_baseline(w, inp_full, budget_s=15.0):
-    """The oracle (untuned, OpenMP over (b, d)) on a bounded sample of the
-    workload: whole batch rows, as many as fit in about ``budget_s``."""
+def algorithmic_valu_slots(N, gate, es):
+    """fp32 VALU issue slots one (b, l, d) element needs on gfx950 without
+    packed instructions, for A of the S4D-real form (A[d,n] = (n+1) A[d,0]) as
+    in every workload here.  A transcendental (exp2, log2, rcp) takes two
+    slots.
+      per state n: A_bar by one multiply (power chain), Delta*u*B (1), state
+                   FMA (1), readout FMA (1)                        -> 4 N
+      per element: widen u, Delta (2 if bf16), bias add (1), softplus (exp,
+                   log: 4 slots, + 2), Delta*u (1), r = exp(Delta A0) (3),
+                   D*u (1), round y (1 if bf16)
+      gate:        widen z (1 if bf16), SiLU (exp, rcp: 4 slots, + 2), y*g (1)
+    """
+    bf = 1 if es == 2 else 0
+    per = 4 * N + 2 * bf + 1 + 6 + 1 + 3 + 1 + bf
+    if gate:
+        per += bf + 6 + 1
+    return per
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_selscan_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
+def load_traffic(workload):
+    try:
+        with open(traffic_file(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("bytes_per_call")
+
+
+def cpu_baseline(w, inp_full, cpu_budget_s=15.0):
+    """The oracle (untuned, OpenMP over (b, d)) on the workload, repeated whole
+    until about ``cpu_budget_s`` seconds of CPU time (all threads) are spent."""
     import oracle
-    import selscan_inputs as si
     threads = oracle.default_threads()
+    elems_per_pass = w.batch * w.L * w.dim
+    c0, t0 = time.process_time(), time.perf_counter()
+    passes = 0
+    while True:
+        oracle.fwd_inputs(inp_full, threads=threads)
+        passes += 1
+        if time.process_time() - c0 >= cpu_budget_s or passes >= 1000:
+            break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {"value": passes * elems_per_pass / wall, "unit": "elements/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full pass(es) of %s (%d elements each), %.1f s wall, %.1f s CPU, "
+                      "fp64 sequential recurrence, OpenMP over (b, d)"
+                      % (passes, w.name, elems_per_pass, wall, cpu)}
 
-    def rows(r0, r1):
-        sl = slice(r0, r1)
-        return si.FwdInputs(dtype=inp_full.dtype, batch=r1 - r0, L=inp_full.L, dim=inp_full.dim,
-                            N=inp_full.N, u=si.Tensor(inp_full.u.value[sl]),
-                            delta=si.Tensor(inp_full.delta.value[sl]),
-                            Bm=si.Tensor(inp_full.Bm.value[sl]), Cm=si.Tensor(inp_full.Cm.value[sl]),
-                            z=None if inp_full.z is None else si.Tensor(inp_full.z.value[sl]),
-                            A=inp_full.A, D_skip=inp_full.D_skip, delta_bias=inp_full.delta_bias)
 
-    t0 = time.perf_counter()
-    oracle.fwd_inputs(rows(0, 1), threads=threads)
-    t1 = time.perf_counter() - t0
-    n_rows = int(max(1, min(w.batch - 1, budget_s / max(t1, 1e-3) - 1)))
-    t0 = time.perf_counter()
-    if n_rows >= 1 and w.batch > 1:
-        oracle.fwd_inputs(rows(1, 1 + n_rows), threads=threads)
-        dt = time.perf_counter() - t0
-        done = n_rows
-    else:
-        dt, done = t1, 1
-    elems = done * w.L * w.dim
-    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d batch rows of %s (%d elements, %.1f s wall, fp64, OpenMP)"
-                      % (done, w.batch, w.name, elems, dt)}
+def make_inputs(w, dev, rotate):
+    import torch
+
+    import selscan_inputs as si
+    inp = si.workload_fwd_inputs(w)
+    base = si.fwd_tensors(inp, dev)
+    sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
+                     for _ in range(rotate - 1)]
+    return inp, sets
+
+
+def pmc_run(w, reps=3):
+    """Workload for the counter runs: one plain 1 GiB device copy (the
+    calibration), then ``reps`` forward calls."""
+    import torch
+
+    import selective_state_space_selscan_amd as ss
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    _, sets = make_inputs(w, dev, 1)
+    t = sets[0]
+    for _ in range(reps):
+        ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                       t["delta_bias"], True, None, return_last_state=w.want_last_state)
+    torch.cuda.synchronize()
+    print("pmc-run done", w.name, reps, flush=True)
+
+
+def parse_pmc(w, fetch_dir, write_dir, reps=3):
+    """Per-call HBM bytes from the two counter runs of ``pmc_run``."""
+    import csv
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        vals = {}
+        for fpath in files:
+            for r in csv.DictReader(open(fpath)):
+                if r["Counter_Name"] == counter:
+                    key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return sorted(vals.items())
+
+    out = {}
+    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = per_kernel(d, counter)
+        # the calibration copy is the largest copyBuffer dispatch (1 GiB)
+        copy = sorted((v for (i, k), v in rows if "copyBuffer" in k), reverse=True)
+        scan = [(k, v) for (i, k), v in rows if "selscan" in k]
+        factor = COPY_CAL_BYTES / (copy[0] * 1024.0) if copy and copy[0] > 0 else None
+        kib_per_call = sum(v for _, v in scan) / reps
+        out[name] = {"counter": counter, "kib_per_call_raw": kib_per_call,
+                     "copy_kib_raw": copy[0] if copy else None, "copy_factor": factor,
+                     "bytes_per_call": None if factor is None else kib_per_call * 1024.0 * factor,
+                     "kernels": sorted({k.split("(")[0] for k, _ in scan})}
+    total = (out["fetch"]["bytes_per_call"] or 0) + (out["write"]["bytes_per_call"] or 0)
+    res = {"workload": w.name, "source_sha256": source_digest(), "bytes_per_call": total,
+           "fetch": out["fetch"], "write": out["write"],
+           "algorithmic_bytes_per_call": algorithmic_bytes(
+               w.batch, w.L, w.dim, w.N, 2 if w.dtype == "bf16" else 4, w.gate,
+               w.want_last_state)}
+    with open(traffic_file(w.name), "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mamba130m_layer")
     ap.add_argument("--rotate", type=int, default=4, help="input-set copies to rotate")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-run", action="store_true")
+    ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+
+    import selscan_inputs as si
+    w = si.WORKLOADS[args.workload]
+    if w.decode_steps:
+        raise SystemExit("bench.py times the forward scan; pick a forward workload")
+    if args.parse_pmc:
+        parse_pmc(w, *args.parse_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the scan shards over (batch, dim) "
               "with no exchange, so multi-GPU throughput is not measured here.", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_run:
+        pmc_run(w)
+        return
 
     import torch
 
-    import selscan_inputs as si
     import selective_state_space_selscan_amd as ss
 
-    w = si.WORKLOADS[args.workload]
-    if w.decode_steps:
-        raise SystemExit("bench.py times the forward scan; pick a forward workload")
     dev = torch.device("cuda:0")
-    inp = si.workload_fwd_inputs(w)
-    base = si.fwd_tensors(inp, dev)
-    sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
-                     for _ in range(args.rotate - 1)]
+    inp, sets = make_inputs(w, dev, args.rotate)
     es = 2 if w.dtype == si.BF16 else 4
-    ys = [torch.empty((w.batch, w.L, w.dim), dtype=base["u"].dtype, device=dev)
+    ys = [torch.empty((w.batch, w.L, w.dim), dtype=sets[0]["u"].dtype, device=dev)
           for _ in range(args.rotate)]
     hls = [torch.empty((w.batch, w.dim, w.N), dtype=torch.float32, device=dev)
            if w.want_last_state else None for _ in range(args.rotate)]
@@ -134,13 +259,15 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    call_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
     elems = w.batch * w.L * w.dim
     ms_per_step = 1e3 * wall / args.steps
-    kernel_ms = float(np.mean(launch_ms))
+    call_mean = float(np.mean(call_ms))
     abytes = algorithmic_bytes(w.batch, w.L, w.dim, w.N, es, w.gate, w.want_last_state)
-    achieved = abytes / (kernel_ms * 1e-3) / 1e9
+    slots = algorithmic_valu_slots(w.N, w.gate, es) * elems
+    achieved = slots / (call_mean * 1e-3) / 1e9
+    peak = VALU_PEAK_SLOTS / 1e9
     result = {
         "metric": "selective-scan fwd elements(B*L*D)/s and HBM GB/s (% of MI355X peak), 1 GPU",
         "value": elems / (ms_per_step * 1e-3),
@@ -159,12 +286,15 @@ def main():
                    "gate": w.gate, "state": "fp32", "rotating_input_sets": args.rotate},
         "hbm_gbps": abytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": abytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "kernel_ms": {"mean": kernel_ms, "p10": float(np.percentile(launch_ms, 10)),
-                      "p50": float(np.median(launch_ms)),
-                      "p90": float(np.percentile(launch_ms, 90))},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "algorithmic_bytes_per_launch": abytes},
+        "call_ms": {"mean": call_mean, "p10": float(np.percentile(call_ms, 10)),
+                    "p50": float(np.median(call_ms)), "p90": float(np.percentile(call_ms, 90))},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
+                     "unit": "G VALU lane-slots/s", "frac": achieved / peak,
+                     "traffic": load_traffic(w.name),
+                     "kernel": "selscan_fwd call (summary pass + main pass)",
+                     "algorithmic_slots_per_element": algorithmic_valu_slots(w.N, w.gate, es),
+                     "algorithmic_bytes_per_call": abytes,
+                     "hbm_gbps_of_call": abytes / (call_mean * 1e-3) / 1e9},
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp)

@@ -10,6 +10,19 @@ import pytest
 
 import selective_state_space_selscan_amd as ss
 
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The validation tests pass fake device addresses.  They are meant for hosts
+# without a GPU: if a check ever regressed, a launch on a GPU would read them.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer tests run only without a GPU")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "selscan.h")
 
@@ -92,6 +105,7 @@ INVALID_FWD = [
 ]
 
 
+@no_gpu_only
 @pytest.mark.parametrize("name,kw,status", INVALID_FWD, ids=[c[0] for c in INVALID_FWD])
 def test_fwd_rejects_invalid_arguments(name, kw, status):
     L = ss.lib()
@@ -99,17 +113,19 @@ def test_fwd_rejects_invalid_arguments(name, kw, status):
     assert L.selscan_last_hip_error() == 0
 
 
+@no_gpu_only
 def test_fwd_workspace_checked_when_needed():
     L = ss.lib()
     need = L.selscan_fwd_workspace_bytes(1, 131072, 2048, 16, 1)
-    if need == 0:
-        pytest.skip("this plan needs no workspace")
-    # every other argument invalid-free except the workspace: use N=5 to be safe?  No:
-    # a too-small workspace must be reported before launching, so pair it with a bad
-    # alignment check order: workspace is checked after N and alignment, before alias.
-    args = fwd_args(batch=1, L=131072, dim=2048, workspace=None, workspace_bytes=0,
-                    dtype=7)
-    assert L.selscan_fwd(*args) == ERR_DTYPE
+    assert need > 0
+    assert L.selscan_fwd_workspace_bytes(1, 131072, 2048, 16, 9) == 0   # invalid dtype
+    assert L.selscan_fwd_workspace_bytes(1, 131072, 2048, 5, 1) == 0    # unsupported N
+    for ws, nbytes in ((None, 0), (fake(12), need - 1)):
+        args = fwd_args(batch=1, L=131072, dim=2048, workspace=ws, workspace_bytes=nbytes)
+        assert L.selscan_fwd(*args) == ERR_WS
+    # misaligned workspace
+    args = fwd_args(batch=1, L=131072, dim=2048, workspace=ctypes.c_void_p(BASE + 12 * STEP + 8))
+    assert L.selscan_fwd(*args) == ERR_UNSUP
 
 
 def step_args(**kw):
@@ -136,6 +152,7 @@ INVALID_STEP = [
 ]
 
 
+@no_gpu_only
 @pytest.mark.parametrize("name,kw,status", INVALID_STEP, ids=[c[0] for c in INVALID_STEP])
 def test_state_update_rejects_invalid_arguments(name, kw, status):
     L = ss.lib()
