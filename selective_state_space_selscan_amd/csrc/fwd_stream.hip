@@ -43,7 +43,11 @@ namespace {
 
 constexpr int kLanes = 64;
 constexpr int kWavesPerBlock = 4;
-constexpr int TT = 8;   // timesteps per prefetch buffer
+constexpr int TT = 4;   // timesteps per prefetch buffer
+// A store offset past the byte range of every output descriptor (a chunk's
+// range is at most TT * dim * 4 bytes, and dim * 4 < 2^26 is checked on the
+// host), so stores from lanes past dim are dropped by the hardware.
+constexpr int kStoreOffsetOutOfRange = 1 << 30;
 
 struct Chunk {
     uint32_t u[TT], x[TT], z[TT];   // raw element bits, widened at use
@@ -52,8 +56,37 @@ struct Chunk {
 struct WaveCtx {
     int64_t b, d0, L, dim, l_begin, l_end;
     int voff, row_bytes;
+    int voff_store;    // voff, or an offset past every descriptor range for lanes past dim
     float bias, Dd, A2_0;
 };
+
+// Raw dwords of one B_t or C_t row (N values, two bf16 or one fp32 per dword).
+template <int N, typename TIO>
+struct RowRaw {
+    static constexpr int W = N * (int)sizeof(TIO) / 4;
+    uint32_t w[W];
+};
+
+template <int N, typename TIO>
+__device__ __forceinline__ void fetch_row(RowRaw<N, TIO> &r, const TIO *p, int64_t row)
+{
+    const const_u32 *q = as_const_u32(p) + row * RowRaw<N, TIO>::W;
+#pragma unroll
+    for (int k = 0; k < RowRaw<N, TIO>::W; ++k)
+        r.w[k] = q[k];
+}
+
+template <int N>
+__device__ __forceinline__ float row_val(const RowRaw<N, float> &r, int n)
+{
+    return __uint_as_float(r.w[n]);
+}
+template <int N>
+__device__ __forceinline__ float row_val(const RowRaw<N, uint16_t> &r, int n)
+{
+    const uint32_t w = r.w[n >> 1];
+    return __uint_as_float((n & 1) ? (w & 0xffff0000u) : (w << 16));
+}
 
 template <bool GATED, typename TIO>
 __device__ __forceinline__ void load_chunk(Chunk &ch, const TIO *u, const TIO *delta, const TIO *z,
@@ -86,88 +119,94 @@ __device__ __forceinline__ void load_chunk(Chunk &ch, const TIO *u, const TIO *d
 
 // TT steps of the recurrence on one prefetched chunk.  FULL: all TT steps are
 // inside the range (no per-step check); otherwise steps past the end are the
-// identity element (Delta = 0).
+// identity element (Delta = 0).  The B_t / C_t rows of step i+1 are fetched
+// (scalar loads) while step i computes.  The loop body has no branch, so the
+// scheduler is free to move loads ahead.
 template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, bool FULL, typename TIO>
 __device__ __forceinline__ void run_chunk(const Chunk &ch, const TIO *Bm, const TIO *Cm, TIO *y,
-                                          const WaveCtx &c, int64_t t0, bool active,
+                                          const WaveCtx &c, int64_t t0,
                                           const float (&A2)[N], float (&h)[N], float &sdelta)
 {
     const int rows = FULL ? TT : (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
     const int64_t elem = (c.b * c.L + t0) * c.dim + c.d0;
     const __amdgpu_buffer_rsrc_t ry =
         make_rsrc(SUMMARY ? nullptr : y + elem, SUMMARY ? 0 : (rows * c.dim - c.d0) * (int64_t)sizeof(TIO));
+    const int64_t row0 = c.b * c.L + t0;
+    const int64_t row_last = c.b * c.L + c.L - 1;
+    RowRaw<N, TIO> bcur, ccur, bnxt, cnxt;
+    fetch_row(bcur, Bm, row0);
+    if (!SUMMARY)
+        fetch_row(ccur, Cm, row0);
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-        const int64_t t = t0 + i;
+        if (i + 1 < TT) {
+            // rows past L are clamped (padding steps, never stored)
+            const int64_t rn = (FULL || row0 + i + 1 <= row_last) ? row0 + i + 1 : row_last;
+            fetch_row(bnxt, Bm, rn);
+            if (!SUMMARY)
+                fetch_row(cnxt, Cm, rn);
+        }
         const bool valid = FULL || i < rows;
-        const int64_t row = c.b * c.L + ((FULL || t < c.L) ? t : c.L - 1);
         const float ut = raw_to_f32(ch.u[i], tag<TIO>());
         const float x = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
         float dt = SOFTPLUS ? softplus(x) : x;
         if (!FULL)
             dt = valid ? dt : 0.0f;        // padding steps are the identity (1, 0)
         const float du = dt * ut;
-        // B_t / C_t rows are read in blocks of NB states to bound SGPR use.
-        constexpr int NB = N < 16 ? N : 16;
         float yv = c.Dd * ut;
         const float r = POW ? hw_exp2(dt * c.A2_0) : 0.0f;
         float pw = 1.0f;
         if (SUMMARY)
             sdelta += dt;
 #pragma unroll
-        for (int n0 = 0; n0 < N; n0 += NB) {
-            float Bv[NB], Cv[NB];
-            load_row<NB>(Bm + n0, row * (N / NB), Bv);
+        for (int n = 0; n < N; ++n) {
+            const float a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
+            h[n] = fmaf(a, h[n], du * row_val<N>(bcur, n));
             if (!SUMMARY)
-                load_row<NB>(Cm + n0, row * (N / NB), Cv);
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                const int n = n0 + k;
-                const float a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
-                h[n] = fmaf(a, h[n], du * Bv[k]);
-                if (!SUMMARY)
-                    yv = fmaf(Cv[k], h[n], yv);
-            }
+                yv = fmaf(row_val<N>(ccur, n), h[n], yv);
         }
         if (!SUMMARY) {
             if (GATED)
                 yv *= silu(raw_to_f32(ch.z[i], tag<TIO>()));
-            // rows past the end fall outside the descriptor; lanes past dim skip
-            if (active)
-                buf_store(ry, c.voff, i * c.row_bytes, yv, y);
+            // rows past the end and lanes past dim fall outside the descriptor
+            buf_store(ry, c.voff_store, i * c.row_bytes, yv, y);
+        }
+        if (i + 1 < TT) {
+            bcur = bnxt;
+            if (!SUMMARY)
+                ccur = cnxt;
         }
     }
 }
 
 template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, typename TIO>
 __device__ __forceinline__ void run_any_chunk(const Chunk &ch, const TIO *Bm, const TIO *Cm, TIO *y,
-                                              const WaveCtx &c, int64_t t0, bool active,
+                                              const WaveCtx &c, int64_t t0,
                                               const float (&A2)[N], float (&h)[N], float &sdelta)
 {
     if (t0 + TT <= c.l_end)
-        run_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, true>(ch, Bm, Cm, y, c, t0, active, A2, h, sdelta);
+        run_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, true>(ch, Bm, Cm, y, c, t0, A2, h, sdelta);
     else
-        run_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, false>(ch, Bm, Cm, y, c, t0, active, A2, h, sdelta);
+        run_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, false>(ch, Bm, Cm, y, c, t0, A2, h, sdelta);
 }
 
 // Forward walk over the part (main pass, and the summary for general A).
 template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, typename TIO>
 __device__ __forceinline__ void run_part(const TIO *u, const TIO *delta, const TIO *z, TIO *y,
                                          const TIO *Bm, const TIO *Cm, const WaveCtx &c,
-                                         bool active, const float (&A2)[N], float (&h)[N],
-                                         float &sdelta)
+                                         const float (&A2)[N], float (&h)[N], float &sdelta)
 {
     Chunk A, B;
     int64_t t0 = c.l_begin;
     load_chunk<GATED>(A, u, delta, z, c, t0);
     for (;;) {
         load_chunk<GATED>(B, u, delta, z, c, t0 + TT);
-        run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW>(A, Bm, Cm, y, c, t0, active, A2, h, sdelta);
+        run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW>(A, Bm, Cm, y, c, t0, A2, h, sdelta);
         t0 += TT;
         if (t0 >= c.l_end)
             break;
         load_chunk<GATED>(A, u, delta, z, c, t0 + TT);
-        run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW>(B, Bm, Cm, y, c, t0, active, A2, h, sdelta);
+        run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW>(B, Bm, Cm, y, c, t0, A2, h, sdelta);
         t0 += TT;
         if (t0 >= c.l_end)
             break;
@@ -273,6 +312,7 @@ __attribute__((amdgpu_waves_per_eu(N <= 16 ? 4 : 1))) void fwd_stream_kernel(
     c.row_bytes = (int)(dim * (int64_t)sizeof(TIO));
     const bool active = c.d0 + lane < dim;
     const int64_t d = active ? c.d0 + lane : dim - 1;
+    c.voff_store = active ? c.voff : kStoreOffsetOutOfRange;
 
     const float A0 = A[d * N];
     bool structured = true;
@@ -307,7 +347,7 @@ __attribute__((amdgpu_waves_per_eu(N <= 16 ? 4 : 1))) void fwd_stream_kernel(
     float sdelta = 0.0f;
     const bool gated = !SUMMARY && z != nullptr;
 #define SELSCAN_RUN(G, SP, PW)                                                                    \
-    run_part<N, SUMMARY, G, SP, PW>(u, delta, z, y, Bm, Cm, c, active, A2, h, sdelta)
+    run_part<N, SUMMARY, G, SP, PW>(u, delta, z, y, Bm, Cm, c, A2, h, sdelta)
     if (SUMMARY && pow_path) {
         if (delta_softplus)
             summary_part_rev<N, true>(u, delta, Bm, c, h, sdelta);

@@ -22,6 +22,10 @@ bool supported_n(int64_t N)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Largest channel count: keeps every per-chunk buffer range and offset of the
+// forward kernels within 32 bits (at most 16 timesteps x dim x 4 bytes < 2^30).
+const int64_t kMaxDim = (int64_t)1 << 24;
+
 // Forward plans.  Default: the streaming kernel.  SELSCAN_FORCE_PLAN=chunked
 // or =serial selects the workgroup-chunked or the one-lane-per-channel kernel
 // (ablations; all three compute the same recurrence).
@@ -123,7 +127,7 @@ int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm
         return SELSCAN_ERR_SHAPE;
     if (!u || !delta || !A || !Bm || !Cm || !y)
         return SELSCAN_ERR_NULL;
-    if (!supported_n(N))
+    if (!supported_n(N) || dim > kMaxDim)
         return SELSCAN_ERR_UNSUPPORTED;
     const void *all[] = {u, delta, A, Bm, Cm, D_skip, z, delta_bias, h0, y, h_last, workspace};
     for (const void *p : all)

@@ -97,6 +97,7 @@ INVALID_FWD = [
     ("y_null", dict(y=None), ERR_NULL),
     ("N5", dict(N=5), ERR_UNSUP),
     ("N128", dict(N=128), ERR_UNSUP),
+    ("dim_too_large", dict(dim=(1 << 24) + 64, batch=1, L=2), ERR_UNSUP),
     ("misaligned_u", dict(u=ctypes.c_void_p(BASE + STEP + 2)), ERR_UNSUP),
     ("misaligned_hlast", dict(h_last=ctypes.c_void_p(BASE + 11 * STEP + 8)), ERR_UNSUP),
     ("y_aliases_u", dict(y=ctypes.c_void_p(BASE + STEP + 64)), ERR_ALIAS),
