@@ -195,6 +195,81 @@ def parse_pmc(w, fetch_dir, write_dir, reps=3):
     print(json.dumps(res))
 
 
+def decode_bytes(batch, dim, N, es, gate):
+    """Bytes one decode step must move: the fp32 state read and written once
+    (8 B per (b, d, n)), u, Delta (and z) read and y written per (b, d), B and C
+    per (b, n), A, D and bias once."""
+    return (batch * dim * N * 8 + batch * dim * ((3 if gate else 2) * es + es)
+            + 2 * batch * N * es + dim * N * 4 + 2 * dim * 4)
+
+
+def bench_decode(w, steps, warmup):
+    """Decode: ``steps`` single-token selscan_state_update calls on the resident
+    fp32 state (batch, dim, N).  Warm: back-to-back steps, the 84 MB state may
+    stay in the 256 MB last-level cache.  Cold: a 1 GiB buffer is written before
+    each timed step, so the state comes from HBM."""
+    import torch
+
+    import selscan_inputs as si
+    import selective_state_space_selscan_amd as ss
+    dev = torch.device("cuda:0")
+    A, D, bias = (torch.from_numpy(x).to(dev) for x in si.decode_params(w))
+    ins = [si.step_tensors(st, w.dtype, dev) for st in si.decode_block(w, 0, 8)]
+    state = torch.zeros((w.batch, w.dim, w.N), dtype=torch.float32, device=dev)
+    ys = [torch.empty((w.batch, w.dim), dtype=ins[0]["u"].dtype, device=dev) for _ in ins]
+    stream = torch.cuda.current_stream(dev)
+    es = 2 if w.dtype == si.BF16 else 4
+
+    def step(i):
+        t = ins[i % len(ins)]
+        ss.selscan_state_update(state, t["u"], t["delta"], A, t["Bm"], t["Cm"], D, t["z"], bias,
+                                True, y=ys[i % len(ins)], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    warm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(min(steps, 50)):
+        flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold_ms = float(np.mean(cold))
+    nb = decode_bytes(w.batch, w.dim, w.N, es, w.gate)
+    elems = w.batch * w.dim
+    res = {
+        "metric": "selective-scan decode step (selscan_state_update) elements(batch*dim)/s, 1 GPU",
+        "value": elems * steps / wall, "unit": "elements/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": 1e3 * wall / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == si.BF16 else "f32",
+        "data": "synthetic (seeded per step)",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "N": w.N,
+                   "state": "fp32 resident"},
+        "step_ms_warm": warm_ms, "step_ms_cold": cold_ms,
+        "roofline": {"bound": "hbm", "achieved": nb / (cold_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": nb / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "state_update_kernel, cold last-level cache",
+                     "algorithmic_bytes_per_step": nb,
+                     "warm_gbps": nb / (warm_ms * 1e-3) / 1e9},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,8 +284,6 @@ def main():
 
     import selscan_inputs as si
     w = si.WORKLOADS[args.workload]
-    if w.decode_steps:
-        raise SystemExit("bench.py times the forward scan; pick a forward workload")
     if args.parse_pmc:
         parse_pmc(w, *args.parse_pmc)
         return
@@ -218,6 +291,9 @@ def main():
         print("bench.py: this build runs on one GPU only; the scan shards over (batch, dim) "
               "with no exchange, so multi-GPU throughput is not measured here.", file=sys.stderr)
         sys.exit(2)
+    if w.decode_steps:
+        bench_decode(w, args.steps, args.warmup)
+        return
     if args.pmc_run:
         pmc_run(w)
         return

@@ -387,13 +387,18 @@ struct StreamPlan {
 };
 
 // SELSCAN_STREAM_PARTS=P overrides the number of sequence parts (tuning knob).
+// Default (measured on MI355X): about 4096 waves (4 per SIMD) when the channel
+// groups are few; with many groups, at least 8 parts (when L allows), since
+// smaller waves balance the tail of the grid better than fewer, longer ones.
 StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim)
 {
     StreamPlan p;
     p.groups = batch * ((dim + kLanes - 1) / kLanes);
-    // About 4 waves per SIMD (256 CUs x 4 SIMDs); parts of at least 4 chunks.
     const int64_t target_waves = 4096;
-    int64_t parts = (target_waves + p.groups / 2) / p.groups;
+    int64_t parts = (target_waves + p.groups - 1) / p.groups;
+    const int64_t min_parts = L / 256 < 8 ? L / 256 : 8;
+    if (parts < min_parts)
+        parts = min_parts;
     const char *e = getenv("SELSCAN_STREAM_PARTS");
     long long ov = 0;
     if (e && sscanf(e, "%lld", &ov) == 1 && ov >= 1)

@@ -5,10 +5,14 @@
 // (Mamba tutorial, pwwt.cn, §5.1 table and §6.3).  The paper walkthrough
 // (m.lqnn.cn) §3.2 names this single-token state update.  The step is
 // HBM-bound: each state entry is read once and written once, 8 bytes per
-// (b, d, n), against 5 flops and one exp2.
+// (b, d, n), against a handful of flops.
 //
-// One lane owns one (b, d) row of N states (N*4 contiguous bytes, loaded as
-// float4).  B and C of row b are wave-uniform.
+// Layout of the work: N/4 consecutive lanes share one (b, d) row of N states,
+// each lane owning one float4 of it, so every state load or store instruction
+// of a wave covers 1 KB of contiguous memory.  Each lane updates its 4 states,
+// forms its part of C.h, and the row's lanes sum the parts with xor-shuffles.
+// The per-row scalars (Delta, u, z) are recomputed by every lane of the row,
+// which costs nothing measurable in a memory-bound step.
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -17,57 +21,91 @@ namespace {
 
 constexpr int kBlock = 256;
 
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float (&v)[4]);
+
+template <>
+__device__ __forceinline__ void load4<float>(const float *p, float (&v)[4])
+{
+    const float4 x = *reinterpret_cast<const float4 *>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t *p, float (&v)[4])
+{
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    v[0] = __uint_as_float(x.x << 16);
+    v[1] = __uint_as_float(x.x & 0xffff0000u);
+    v[2] = __uint_as_float(x.y << 16);
+    v[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
 template <int N, typename T>
 __global__ __launch_bounds__(kBlock) void state_update_kernel(
     float *__restrict__ state, const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ A, const T *__restrict__ Bm, const T *__restrict__ Cm,
     const float *__restrict__ D_skip, const T *__restrict__ z,
-    const float *__restrict__ delta_bias, int delta_softplus, T *__restrict__ y, int64_t dim)
+    const float *__restrict__ delta_bias, int delta_softplus, T *__restrict__ y, int64_t dim,
+    int64_t rows)
 {
-    static_assert(N % 4 == 0, "N must be a multiple of 4");
-    const int64_t b = blockIdx.y;
-    const int64_t d = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (d >= dim)
-        return;
-    const int64_t e = b * dim + d;
-    float4 *row = reinterpret_cast<float4 *>(state + e * N);
-    const T *Bt = Bm + b * N;
-    const T *Ct = Cm + b * N;
+    static_assert(N % 4 == 0 && kBlock % (N / 4) == 0, "N/4 lanes per row");
+    constexpr int R = N / 4;                       // lanes per (b, d) row
+    const int64_t gt = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t row = gt / R;
+    const int q = (int)(gt % R);                   // this lane's float4 of the row
+    const bool valid = row < rows;
+    const int64_t r = valid ? row : rows - 1;      // tail lanes compute on a valid row
+    const int64_t b = r / dim;
+    const int64_t d = r - b * dim;
 
-    const float ut = load_elem(u, e);
-    const float x = load_elem(delta, e) + (delta_bias ? delta_bias[d] : 0.0f);
+    float4 *srow = reinterpret_cast<float4 *>(state + r * N) + q;
+    const float4 h4 = *srow;
+    const float4 a4 = *reinterpret_cast<const float4 *>(A + d * N + 4 * q);
+    float Bv[4], Cv[4];
+    load4<T>(Bm + b * N + 4 * q, Bv);
+    load4<T>(Cm + b * N + 4 * q, Cv);
+
+    const float ut = load_elem(u, r);
+    const float x = load_elem(delta, r) + (delta_bias ? delta_bias[d] : 0.0f);
     const float dt = delta_softplus ? softplus(x) : x;
     const float du = dt * ut;
     const float dA = dt * kLog2e;
+    float h[4] = {h4.x, h4.y, h4.z, h4.w};
+    const float a[4] = {a4.x, a4.y, a4.z, a4.w};
     float acc = 0.0f;
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-        float4 hv = row[q];
-        float4 av = *reinterpret_cast<const float4 *>(A + d * N + 4 * q);
-        float hs[4] = {hv.x, hv.y, hv.z, hv.w};
-        float as[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int n = 4 * q + k;
-            hs[k] = fmaf(hw_exp2(dA * as[k]), hs[k], du * load_elem(Bt, n));
-            acc = fmaf(load_elem(Ct, n), hs[k], acc);
-        }
-        row[q] = make_float4(hs[0], hs[1], hs[2], hs[3]);
+    for (int k = 0; k < 4; ++k) {
+        h[k] = fmaf(hw_exp2(dA * a[k]), h[k], du * Bv[k]);
+        acc = fmaf(Cv[k], h[k], acc);
     }
-    float yv = fmaf(D_skip ? D_skip[d] : 0.0f, ut, acc);
-    if (z)
-        yv *= silu(load_elem(z, e));
-    store_elem(y, e, yv);
+    // sum C.h over the R lanes of the row (all lanes take part)
+#pragma unroll
+    for (int off = R / 2; off > 0; off >>= 1)
+        acc += __shfl_xor(acc, off, R);
+    if (valid) {
+        *srow = make_float4(h[0], h[1], h[2], h[3]);
+        if (q == 0) {
+            float yv = fmaf(D_skip ? D_skip[d] : 0.0f, ut, acc);
+            if (z)
+                yv *= silu(load_elem(z, r));
+            store_elem(y, r, yv);
+        }
+    }
 }
 
 template <int N, typename T>
 hipError_t launch_typed(const StepArgs &a, hipStream_t stream)
 {
-    dim3 grid((unsigned)((a.dim + kBlock - 1) / kBlock), (unsigned)a.batch);
-    hipLaunchKernelGGL((state_update_kernel<N, T>), grid, dim3(kBlock), 0, stream, a.state,
-                       (const T *)a.u, (const T *)a.delta, a.A, (const T *)a.Bm,
-                       (const T *)a.Cm, a.D_skip, (const T *)a.z, a.delta_bias,
-                       a.delta_softplus, (T *)a.y, a.dim);
+    const int64_t rows = a.batch * a.dim;
+    const int64_t threads = rows * (N / 4);
+    const int64_t blocks = (threads + kBlock - 1) / kBlock;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((state_update_kernel<N, T>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, a.state, (const T *)a.u, (const T *)a.delta, a.A,
+                       (const T *)a.Bm, (const T *)a.Cm, a.D_skip, (const T *)a.z, a.delta_bias,
+                       a.delta_softplus, (T *)a.y, a.dim, rows);
     return hipGetLastError();
 }
 
