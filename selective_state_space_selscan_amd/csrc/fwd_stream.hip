@@ -43,15 +43,18 @@ namespace {
 
 constexpr int kLanes = 64;
 constexpr int kWavesPerBlock = 4;
-constexpr int TT = 4;   // timesteps per prefetch buffer
+constexpr int TT = 4;   // timesteps per prefetch buffer, main pass
+constexpr int TTS = 8;  // timesteps per prefetch buffer, summary pass
 // A store offset past the byte range of every output descriptor (a chunk's
 // range is at most TT * dim * 4 bytes, and dim * 4 < 2^26 is checked on the
 // host), so stores from lanes past dim are dropped by the hardware.
 constexpr int kStoreOffsetOutOfRange = 1 << 30;
 
-struct Chunk {
-    uint32_t u[TT], x[TT], z[TT];   // raw element bits, widened at use
+template <int TTc>
+struct ChunkT {
+    uint32_t u[TTc], x[TTc], z[TTc];   // raw element bits, widened at use
 };
+using Chunk = ChunkT<TT>;
 
 struct WaveCtx {
     int64_t b, d0, L, dim, l_begin, l_end;
@@ -88,10 +91,11 @@ __device__ __forceinline__ float row_val(const RowRaw<N, uint16_t> &r, int n)
     return __uint_as_float((n & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-template <bool GATED, typename TIO>
-__device__ __forceinline__ void load_chunk(Chunk &ch, const TIO *u, const TIO *delta, const TIO *z,
-                                           const WaveCtx &c, int64_t t0)
+template <bool GATED, int TTc, typename TIO>
+__device__ __forceinline__ void load_chunk(ChunkT<TTc> &ch, const TIO *u, const TIO *delta,
+                                           const TIO *z, const WaveCtx &c, int64_t t0)
 {
+    constexpr int TT = TTc;
     int64_t rows = c.l_end - t0;
     rows = rows < 0 ? 0 : (rows > TT ? TT : rows);
     if (t0 < c.l_begin)
@@ -219,34 +223,36 @@ __device__ __forceinline__ void run_part(const TIO *u, const TIO *delta, const T
 // is one running product and Delta_t u_t Q_t^(n+1) one multiply per n, so a
 // (t, n) costs a multiply and an FMA (the forward walk needs three ops).
 template <int N, bool SOFTPLUS, bool FULL, typename TIO>
-__device__ __forceinline__ void summary_chunk_rev(const Chunk &ch, const TIO *Bm, const WaveCtx &c,
-                                                  int64_t t0, float &Q, float (&x)[N],
-                                                  float &sdelta)
+__device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const TIO *Bm,
+                                                  const WaveCtx &c, int64_t t0, float &Q,
+                                                  float (&x)[N], float &sdelta)
 {
+    constexpr int TT = TTS;
     const int rows = FULL ? TT : (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
-    constexpr int NB = N < 16 ? N : 16;
+    const int64_t row0 = c.b * c.L + t0;
+    // B_t row of step i-1 is fetched (scalar loads) while step i computes.
+    RowRaw<N, TIO> bcur, bnxt;
+    fetch_row(bcur, Bm, row0 + (FULL ? TT - 1 : rows - 1));
 #pragma unroll
     for (int i = TT - 1; i >= 0; --i) {
         if (!FULL && i >= rows)
             continue;   // uniform: steps past the end contribute nothing
-        const int64_t row = c.b * c.L + t0 + i;
+        if (i > 0)
+            fetch_row(bnxt, Bm, row0 + i - 1);
         const float ut = raw_to_f32(ch.u[i], tag<TIO>());
         const float xr = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
         const float dt = SOFTPLUS ? softplus(xr) : xr;
         sdelta += dt;
         float g = dt * ut * Q;
 #pragma unroll
-        for (int n0 = 0; n0 < N; n0 += NB) {
-            float Bv[NB];
-            load_row<NB>(Bm + n0, row * (N / NB), Bv);
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                if (n0 + k)
-                    g *= Q;
-                x[n0 + k] = fmaf(g, Bv[k], x[n0 + k]);
-            }
+        for (int n = 0; n < N; ++n) {
+            if (n)
+                g *= Q;
+            x[n] = fmaf(g, row_val<N>(bcur, n), x[n]);
         }
         Q *= hw_exp2(dt * c.A2_0);
+        if (i > 0)
+            bcur = bnxt;
     }
 }
 
@@ -254,8 +260,9 @@ template <int N, bool SOFTPLUS, typename TIO>
 __device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta, const TIO *Bm,
                                                  const WaveCtx &c, float (&x)[N], float &sdelta)
 {
+    constexpr int TT = TTS;
     const int64_t nchunks = (c.l_end - c.l_begin + TT - 1) / TT;
-    Chunk A, B;
+    ChunkT<TTS> A, B;
     float Q = 1.0f;
     int64_t k = nchunks - 1;
     int64_t t0 = c.l_begin + k * TT;

@@ -243,3 +243,28 @@ def test_state_update_ragged_and_small_n(device):
         torch.cuda.synchronize()
         assert rel_err(to_np(y), ey) <= TOL["f32"]
         assert rel_err(to_np(gs), os_) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+@pytest.mark.parametrize("N,L", [(4, 700), (16, 3000), (32, 1000), (64, 600)])
+def test_unstructured_A(device, N, L, dtype):
+    """A with no (n+1) A[d,0] structure runs the exp2 path.  Channels 0..63
+    are fully random, the next group is S4D-real except for one channel, so
+    one wave mixes both (it must take the exp2 path), and the last group is
+    S4D-real (power path).  L is long enough for several sequence parts."""
+    dim = 192
+    inp = si.make_fwd_inputs(2, L, dim, N, dtype, True, seed=200 + N, h0=True, D_value=None)
+    rng = np.random.default_rng(300 + N)
+    A = inp.A.copy()
+    A[:64] = -rng.uniform(0.05, 2.0, size=(64, N)).astype(np.float32)
+    A[64 + 5, N - 1] *= np.float32(1.0001)
+    inp.A = np.ascontiguousarray(A)
+    check_fwd(inp, device, what="unstructured A N%d" % N)
+
+
+def test_unstructured_A_long_parts(device):
+    """Random A, long sequence: the fold of part summaries uses exp2(A S)."""
+    inp = si.make_fwd_inputs(1, 20000, 128, 16, si.BF16, True, seed=17, h0=True, D_value=0.0)
+    rng = np.random.default_rng(18)
+    inp.A = (-rng.uniform(0.02, 1.0, size=(128, 16))).astype(np.float32)
+    check_fwd(inp, device, channels=sample_channels(128, 32), what="unstructured A long")
