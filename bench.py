@@ -274,7 +274,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mamba130m_layer")
     ap.add_argument("--rotate", type=int, default=4, help="input-set copies to rotate")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

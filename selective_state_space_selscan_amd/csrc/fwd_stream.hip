@@ -342,12 +342,24 @@ __attribute__((amdgpu_waves_per_eu(N <= 16 ? 4 : 1))) void fwd_stream_kernel(
     for (int n = 0; n < N; ++n)
         h[n] = (!SUMMARY && h0) ? h0[(c.b * dim + d) * N + n] : 0.0f;
     if (!SUMMARY) {
+        // h <- exp(A S) h + x for each earlier part (S = its sum of Delta, x =
+        // its end state from zero); for structured A, exp(A[d,n] S) = e^(n+1).
         for (int q = 0; q < part; ++q) {
             const float *s = summ + ((grp * (parts - 1) + q) * (N + 1)) * kLanes + lane;
             const float S = s[0];
+            if (pow_path) {
+                const float e = hw_exp2(c.A2_0 * S);
+                float pw = 1.0f;
 #pragma unroll
-            for (int n = 0; n < N; ++n)
-                h[n] = fmaf(hw_exp2(A2[n] * S), h[n], s[(n + 1) * kLanes]);
+                for (int n = 0; n < N; ++n) {
+                    pw *= e;
+                    h[n] = fmaf(pw, h[n], s[(n + 1) * kLanes]);
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    h[n] = fmaf(hw_exp2(A2[n] * S), h[n], s[(n + 1) * kLanes]);
+            }
         }
     }
 
