@@ -10,7 +10,10 @@ header for the page citations).  ``build()`` compiles it with gcc + OpenMP;
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (LTI convolution, closed-form double sum, associative scan, Delta limits,
 softplus round trip, skip path, split invariance, decode = forward,
-causality, permutation and linearity).  The pages print no worked numeric
+causality, permutation and linearity); the variants of ``fwd`` by the LTI
+convolution with the exact zero-order-hold kernel, its A -> 0 limit, the
+suffix closed form of the reverse direction, torch's conv1d for the conv
+prologue and the flip identity of the reverse direction.  The pages print no worked numeric
 example, so no value is pinned to a number printed on the pages.
 """
 from __future__ import annotations
@@ -49,6 +52,9 @@ def _load():
         lib.oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
                                    I64, I64, I64, I64, ctypes.c_int]
         lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
+                                      I64, I64, I64, I64, ctypes.c_int, P, P, I64, ctypes.c_int]
+        lib.oracle_fwd_ex.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P,
                                             I64, I64, I64, ctypes.c_int]
         lib.oracle_state_update.restype = ctypes.c_int
@@ -71,15 +77,24 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
+ZOH_EXACT = 1
+REVERSE = 2
+
+
 def fwd(u, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None, delta_softplus=True,
-        h0=None, threads: Optional[int] = None):
+        h0=None, threads: Optional[int] = None, flags: int = 0, conv_w=None, conv_b=None):
     """Sequential fp64 forward scan.
 
     u, delta, z: (batch, L, dim); Bm, Cm: (batch, L, N); A: (dim, N);
     D_skip, delta_bias: (dim,); h0: (batch, dim, N).
+    flags: ZOH_EXACT and/or REVERSE.  conv_w (dim, k), conv_b (dim,): causal
+    depthwise conv1d + SiLU prologue applied to u (then u is the conv input).
     Returns (y (batch, L, dim) float64, h_last (batch, dim, N) float64)."""
     u, delta, A, Bm, Cm = map(_f32, (u, delta, A, Bm, Cm))
     D_skip, z, delta_bias = map(_f32, (D_skip, z, delta_bias))
+    conv_w, conv_b = _f32(conv_w), _f32(conv_b)
+    conv_k = 0 if conv_w is None else conv_w.shape[1]
+    assert conv_w is None or conv_w.shape == (u.shape[2], conv_k)
     batch, L, dim = u.shape
     N = A.shape[1]
     assert delta.shape == u.shape and A.shape == (dim, N)
@@ -89,10 +104,11 @@ def fwd(u, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None, delta_softplu
     assert h0a is None or h0a.shape == (batch, dim, N)
     y = np.empty((batch, L, dim), dtype=np.float64)
     h_last = np.empty((batch, dim, N), dtype=np.float64)
-    rc = _load().oracle_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip),
-                            _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0a),
-                            _ptr(y), _ptr(h_last), batch, L, dim, N,
-                            threads or default_threads())
+    rc = _load().oracle_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                               _ptr(D_skip), _ptr(z), _ptr(delta_bias),
+                               int(bool(delta_softplus)), _ptr(h0a), _ptr(y), _ptr(h_last),
+                               batch, L, dim, N, int(flags), _ptr(conv_w), _ptr(conv_b),
+                               conv_k, threads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_fwd failed with code %d" % rc)
     return y, h_last
@@ -119,8 +135,9 @@ def state_update(state, u, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=Non
     return y
 
 
-def fwd_inputs(inp, h0=None, threads=None):
+def fwd_inputs(inp, h0=None, threads=None, flags=0, conv_w=None, conv_b=None):
     """Run ``fwd`` on a ``selscan_inputs.FwdInputs`` bundle."""
     return fwd(inp.u.value, inp.delta.value, inp.A, inp.Bm.value, inp.Cm.value, inp.D_skip,
                None if inp.z is None else inp.z.value, inp.delta_bias, True,
-               inp.h0 if h0 is None else h0, threads=threads)
+               inp.h0 if h0 is None else h0, threads=threads, flags=flags, conv_w=conv_w,
+               conv_b=conv_b)

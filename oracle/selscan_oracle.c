@@ -28,6 +28,22 @@
  *  - same tutorial, §5.1 table and §6.3: decode keeps one fixed-size state per
  *    sample and advances it by O(1) work per token.
  *
+ * Variants (oracle_fwd_ex), from the same pages:
+ *  - exact zero-order hold: B_bar = (exp(Delta A) - 1) / A * B (tutorial §2.2,
+ *    selection-mechanism article discosf.com §2.1) instead of Delta * B; for
+ *    A = 0 the limit Delta * B;
+ *  - reverse direction: the whole forward applied to the time-reversed
+ *    sequence, output in the original order, i.e. the recurrence runs from
+ *    t = L-1 down to 0, h_t = A_bar_t h_{t+1} + B_bar_t u_t (the bidirectional
+ *    scan of the tutorial's §7 outlook); h0 is the state entering t = L-1,
+ *    h_last the state after t = 0, and the conv prologue is causal in the
+ *    reversed time;
+ *  - causal depthwise conv1d + SiLU prologue (tutorial §3.3 and the §4.2
+ *    listing: Conv1d(groups=d_inner, padding=k-1) sliced to the first L
+ *    outputs, then SiLU): the scan input is
+ *    u[b,t,d] = SiLU(sum_j w[d,j] * x[b, t-(k-1)+j, d] + conv_bias[d]),
+ *    with x = 0 before t = 0, and the skip term D*u uses that u.
+ *
  * Parity pins: this file is checked against closed forms and identities in
  * tests/test_oracle_pins.py, never against the HIP path.
  *
@@ -59,24 +75,41 @@ static double step_delta(double raw, const float *delta_bias, int64_t d, int del
     return delta_softplus ? softplus(x) : x;
 }
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }
+
+enum { ORACLE_ZOH_EXACT = 1, ORACLE_REVERSE = 2 };
+
+/* Delta * B_bar / B for one state: Delta (Euler form) or expm1(Delta A) / A. */
+static double bbar_coeff(double dt, double a, int zoh_exact)
+{
+    if (!zoh_exact)
+        return dt;
+    if (a == 0.0)
+        return dt;
+    return expm1(dt * a) / a;
+}
 
 /*
  * u, delta, z: (batch, L, dim); Bm, Cm: (batch, L, N); A: (dim, N);
  * D_skip, delta_bias: (dim) or NULL; z NULL means no gate;
  * h0: (batch, dim, N) double or NULL (zeros);
  * y: (batch, L, dim) double, written; h_last: (batch, dim, N) double or NULL.
+ * flags: ORACLE_ZOH_EXACT, ORACLE_REVERSE.  conv_w: (dim, conv_k) or NULL
+ * (no prologue; u is the scan input), conv_b: (dim) or NULL.
  */
-int oracle_fwd(const float *u, const float *delta, const float *A,
-               const float *Bm, const float *Cm, const float *D_skip,
-               const float *z, const float *delta_bias, int delta_softplus,
-               const double *h0, double *y, double *h_last,
-               int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads)
+int oracle_fwd_ex(const float *u, const float *delta, const float *A,
+                  const float *Bm, const float *Cm, const float *D_skip,
+                  const float *z, const float *delta_bias, int delta_softplus,
+                  const double *h0, double *y, double *h_last,
+                  int64_t batch, int64_t L, int64_t dim, int64_t N, int flags,
+                  const float *conv_w, const float *conv_b, int64_t conv_k, int nthreads)
 {
-    if (batch < 1 || L < 0 || dim < 1 || N < 1)
+    if (batch < 1 || L < 0 || dim < 1 || N < 1 || (conv_w && conv_k < 1))
         return 1;
     if (nthreads > 0)
         omp_set_num_threads(nthreads);
+    const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
+    const int rev = (flags & ORACLE_REVERSE) != 0;
     int64_t pairs = batch * dim;
     int bad = 0;
 #pragma omp parallel
@@ -91,16 +124,32 @@ int oracle_fwd(const float *u, const float *delta, const float *A,
                 int64_t b = p / dim, d = p % dim;
                 for (int64_t n = 0; n < N; ++n)
                     h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
-                for (int64_t t = 0; t < L; ++t) {
+                for (int64_t s = 0; s < L; ++s) {
+                    int64_t t = rev ? L - 1 - s : s;
                     int64_t e = (b * L + t) * dim + d;      /* (b, t, d) */
                     const float *Bt = Bm + (b * L + t) * N;  /* (b, t, :) */
                     const float *Ct = Cm + (b * L + t) * N;
                     double dt = step_delta((double)delta[e], delta_bias, d, delta_softplus);
-                    double ut = (double)u[e];
+                    double ut;
+                    if (conv_w) {
+                        /* causal along the scan direction: taps reach back
+                           (forward) or ahead (reverse) in the original axis */
+                        double acc = conv_b ? (double)conv_b[d] : 0.0;
+                        for (int64_t j = 0; j < conv_k; ++j) {
+                            int64_t tt = rev ? t + (conv_k - 1) - j : t - (conv_k - 1) + j;
+                            if (tt >= 0 && tt < L)
+                                acc += (double)conv_w[d * conv_k + j] *
+                                       (double)u[(b * L + tt) * dim + d];
+                        }
+                        ut = silu(acc);
+                    } else {
+                        ut = (double)u[e];
+                    }
                     double acc = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
-                        double a_bar = exp(dt * (double)A[d * N + n]);
-                        double bu = dt * (double)Bt[n] * ut;
+                        double an = (double)A[d * N + n];
+                        double a_bar = exp(dt * an);
+                        double bu = bbar_coeff(dt, an, zoh) * (double)Bt[n] * ut;
                         h[n] = a_bar * h[n] + bu;
                         acc += (double)Ct[n] * h[n];
                     }
@@ -117,6 +166,16 @@ int oracle_fwd(const float *u, const float *delta, const float *A,
         }
     }
     return bad ? 2 : 0;
+}
+
+int oracle_fwd(const float *u, const float *delta, const float *A,
+               const float *Bm, const float *Cm, const float *D_skip,
+               const float *z, const float *delta_bias, int delta_softplus,
+               const double *h0, double *y, double *h_last,
+               int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads)
+{
+    return oracle_fwd_ex(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, y,
+                         h_last, batch, L, dim, N, 0, NULL, NULL, 0, nthreads);
 }
 
 /*

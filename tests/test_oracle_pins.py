@@ -384,3 +384,131 @@ def test_oracle_regression_fixture():
     y, h = oracle.fwd_inputs(inp, threads=1)
     assert np.max(np.abs(y.ravel() - np.array(g["y"]))) <= 1e-15 * np.max(np.abs(g["y"]))
     assert np.max(np.abs(h.ravel() - np.array(g["h_last"]))) <= 1e-15 * np.max(np.abs(g["h_last"]))
+
+
+# ----------------------------------------------------------------------------
+# Variants: exact zero-order hold, reverse direction, conv1d + SiLU prologue
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_zoh_exact_lti_equals_convolution(with_h0):
+    """Exact ZOH (tutorial §2.2): B_bar = (exp(Delta A) - 1) / A * B.  In the
+    LTI case y is the convolution with K_k = C A_bar^k B_bar (tutorial §2.3)."""
+    batch, L, dim, N = 1, 40, 3, 4
+    u, _, A, _, _, D, _, bias, h0 = rng_inputs(31, batch, L, dim, N)
+    rng = np.random.default_rng(32)
+    c = rng.uniform(-1.0, 2.0, size=(batch, 1, dim)).astype(np.float32)
+    delta = np.broadcast_to(c, (batch, L, dim)).copy()
+    Bv = rng.standard_normal((batch, 1, N)).astype(np.float32)
+    Cv = rng.standard_normal((batch, 1, N)).astype(np.float32)
+    Bm = np.broadcast_to(Bv, (batch, L, N)).copy()
+    Cm = np.broadcast_to(Cv, (batch, L, N)).copy()
+    y, _ = oracle.fwd(u, delta, A, Bm, Cm, D, None, bias, True, h0=h0 if with_h0 else None,
+                      flags=oracle.ZOH_EXACT)
+    dt = softplus_lib(c[0, 0].astype(np.float64) + bias)
+    expect = np.zeros((batch, L, dim))
+    for d in range(dim):
+        An = A[d].astype(np.float64)
+        Abar = np.exp(dt[d] * An)
+        Bbar = (Abar - 1.0) / An * Bv[0, 0].astype(np.float64)       # textbook ZOH
+        Cb = Cv[0, 0].astype(np.float64)
+        K = np.array([np.sum(Cb * Abar ** k * Bbar) for k in range(L)])
+        for t in range(L):
+            acc = sum(K[k] * float(u[0, t - k, d]) for k in range(t + 1))
+            if with_h0:
+                acc += np.sum(Cb * Abar ** (t + 1) * h0[0, d].astype(np.float64))
+            expect[0, t, d] = acc + float(D[d]) * float(u[0, t, d])
+    assert rel(y, expect) < 1e-11
+
+
+def test_zoh_exact_small_A_tends_to_euler():
+    batch, L, dim, N = 2, 30, 3, 4
+    u, delta, _, Bm, Cm, D, z, bias, h0 = rng_inputs(33, batch, L, dim, N)
+    A = np.full((dim, N), -1e-9, np.float32)
+    y1, h1 = oracle.fwd(u, delta, A, Bm, Cm, D, z, bias, True, h0=h0, flags=oracle.ZOH_EXACT)
+    y2, h2 = oracle.fwd(u, delta, A, Bm, Cm, D, z, bias, True, h0=h0)
+    assert rel(y1, y2) < 1e-7 and rel(h1, h2) < 1e-7
+    # and for larger |Delta A| the two discretisations differ
+    A2 = np.full((dim, N), -2.0, np.float32)
+    y3, _ = oracle.fwd(u, delta, A2, Bm, Cm, D, z, bias, True, flags=oracle.ZOH_EXACT)
+    y4, _ = oracle.fwd(u, delta, A2, Bm, Cm, D, z, bias, True)
+    assert rel(y3, y4) > 1e-3
+
+
+def test_reverse_equals_suffix_closed_form():
+    """Reverse direction: h_t = A_bar_t h_{t+1} + Delta_t B_t u_t, whose closed
+    form is h_t = sum_{s>=t} exp(A sum_{k=t}^{s-1} Delta_k) Delta_s B_s u_s
+    + exp(A sum_{k>=t} Delta_k) h0."""
+    batch, L, dim, N = 1, 30, 3, 5
+    u, delta, A, Bm, Cm, D, z, bias, h0 = rng_inputs(34, batch, L, dim, N)
+    y, hL = oracle.fwd(u, delta, A, Bm, Cm, D, z, bias, True, h0=h0, flags=oracle.REVERSE)
+    dt = softplus_lib(delta.astype(np.float64) + bias)[0]          # (L, dim)
+    ey = np.zeros((L, dim))
+    eh = np.zeros((dim, N))
+    for d in range(dim):
+        An = A[d].astype(np.float64)
+        for t in range(L):
+            h = np.exp(An * dt[t:, d].sum()) * h0[0, d].astype(np.float64)
+            for s_ in range(t, L):
+                h = h + np.exp(An * dt[t:s_, d].sum()) * dt[s_, d] \
+                    * Bm[0, s_].astype(np.float64) * float(u[0, s_, d])
+            ey[t, d] = (np.dot(Cm[0, t].astype(np.float64), h) + float(D[d]) * float(u[0, t, d])) \
+                * silu_lib(float(z[0, t, d]))
+            if t == 0:
+                eh[d] = h
+    assert rel(y[0], ey) < 1e-11
+    assert rel(hL[0], eh) < 1e-11
+
+
+def conv_lib(x, w, b):
+    """Causal depthwise conv1d + SiLU with torch (fp64, CPU): Conv1d with
+    groups = channels and padding k-1, first L outputs (tutorial §4.2)."""
+    import torch
+    L = x.shape[1]
+    xt = torch.from_numpy(x.astype(np.float64)).transpose(1, 2)            # (b, d, L)
+    wt = torch.from_numpy(w.astype(np.float64))[:, None, :]                 # (d, 1, k)
+    bt = None if b is None else torch.from_numpy(b.astype(np.float64))
+    out = torch.nn.functional.conv1d(xt, wt, bt, padding=w.shape[1] - 1, groups=w.shape[0])
+    out = out[..., :L].transpose(1, 2).numpy()
+    return out * expit(out)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_conv_prologue_matches_torch_conv1d(k):
+    """With B = 0 only the skip path remains: y = D * u_conv * SiLU(z), where
+    u_conv is torch's causal depthwise conv1d followed by SiLU."""
+    batch, L, dim, N = 2, 17, 5, 4
+    x, delta, A, Bm, Cm, D, z, bias, _ = rng_inputs(40 + k, batch, L, dim, N)
+    rng = np.random.default_rng(50 + k)
+    w = rng.standard_normal((dim, k)).astype(np.float32)
+    cb = rng.standard_normal(dim).astype(np.float32)
+    y, _ = oracle.fwd(x, delta, A, np.zeros_like(Bm), Cm, D, z, bias, True, conv_w=w, conv_b=cb)
+    uc = conv_lib(x, w, cb)
+    ey = D.astype(np.float64) * uc * silu_lib(z)
+    assert rel(y, ey) < 1e-13
+
+
+def test_conv_prologue_then_scan():
+    """The conv output feeds the scan exactly like a precomputed u."""
+    batch, L, dim, N = 2, 25, 4, 6
+    x, delta, A, Bm, Cm, D, z, bias, h0 = rng_inputs(60, batch, L, dim, N)
+    rng = np.random.default_rng(61)
+    w = rng.standard_normal((dim, 4)).astype(np.float32)
+    y, hL = oracle.fwd(x, delta, A, Bm, Cm, D, z, bias, True, h0=h0, conv_w=w)
+    uc = conv_lib(x, w, None).astype(np.float32)                            # rounded to fp32
+    y2, h2 = oracle.fwd(uc, delta, A, Bm, Cm, D, z, bias, True, h0=h0)
+    assert rel(y, y2) < 1e-6 and rel(hL, h2) < 1e-6
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_reverse_is_forward_on_flipped_sequence(flags):
+    """REVERSE computes the forward (conv prologue included) on the
+    time-reversed sequence and returns it in the original order."""
+    batch, L, dim, N = 2, 23, 4, 5
+    x, delta, A, Bm, Cm, D, z, bias, h0 = rng_inputs(62, batch, L, dim, N)
+    w = np.random.default_rng(63).standard_normal((dim, 3)).astype(np.float32)
+    f = lambda a: np.ascontiguousarray(a[:, ::-1])
+    y, hL = oracle.fwd(x, delta, A, Bm, Cm, D, z, bias, True, h0=h0, conv_w=w,
+                       flags=flags | oracle.REVERSE)
+    yf, hf = oracle.fwd(f(x), f(delta), A, f(Bm), f(Cm), D, f(z), bias, True, h0=h0, conv_w=w,
+                        flags=flags)
+    assert np.array_equal(y, f(yf)) and np.array_equal(hL, hf)
