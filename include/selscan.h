@@ -17,6 +17,14 @@
  *                        §2.4 (the state h of shape (B,L,D,N) is never written
  *                        to HBM; only y of shape (B,L,D) is).
  *
+ *  selscan_fwd_ex        the same forward with the variants the pages describe:
+ *                        exact zero-order hold B_bar = (exp(Delta A) - 1) / A * B
+ *                        (tutorial §2.2, selection-mechanism article discosf.com
+ *                        §2.1), the reverse scan direction (the bidirectional use of
+ *                        the tutorial's §7 outlook) and the causal depthwise
+ *                        conv1d + SiLU that precedes the scan in the Mamba block
+ *                        (tutorial §3.3 and its §4.2 listing), fused as a prologue.
+ *
  *  selscan_state_update  one decode step of the same recurrence on a resident
  *                        state: constant memory and O(1) work per token, one
  *                        state per sample.  Sources: Mamba tutorial §5.1 table
@@ -69,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 1
+#define SELSCAN_ABI_VERSION 2
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -135,6 +143,50 @@ int selscan_fwd(const void *u, const void *delta, const float *A,
                 const float *h0, void *y, float *h_last,
                 int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Flags of selscan_fwd_ex. */
+#define SELSCAN_FLAG_ZOH_EXACT 1   /* B_bar = (exp(Delta A) - 1) / A * B, Delta B where A = 0 */
+#define SELSCAN_FLAG_REVERSE   2   /* scan from t = L-1 down to t = 0                      */
+#define SELSCAN_MAX_CONV_WIDTH 4
+
+/*
+ * Selective-scan forward with variants.  Arguments as selscan_fwd, plus:
+ *
+ *   flags        0 or an OR of SELSCAN_FLAG_ZOH_EXACT, SELSCAN_FLAG_REVERSE.
+ *                ZOH_EXACT: the state update is
+ *                  h = exp(Delta A) h + (exp(Delta A) - 1) / A * B u
+ *                instead of h = exp(Delta A) h + Delta B u (the limit Delta B u
+ *                where A[d,n] = 0).
+ *                REVERSE: the whole computation runs on the time-reversed
+ *                sequence and y is returned in the original order: the
+ *                recurrence is h_t = A_bar_t h_{t+1} + B_bar_t u_t from t = L-1
+ *                down to 0, h0 is the state entering t = L-1 and h_last the
+ *                state after t = 0.  The conv prologue is then causal in the
+ *                reversed time (its taps reach t+1 .. t+k-1).
+ *   conv_weight  (dim, conv_width) fp32, depthwise causal conv taps; used when
+ *                conv_width > 0, and then required.
+ *   conv_bias    (dim) fp32 or NULL (0).
+ *   conv_width   0: no prologue, u is the scan input (conv_weight and conv_bias
+ *                are ignored).  1..SELSCAN_MAX_CONV_WIDTH: the scan input is
+ *                  u'[b,t,d] = SiLU(conv_bias[d] + sum_j conv_weight[d,j] *
+ *                                   u[b, t-(conv_width-1)+j, d])
+ *                with u = 0 before t = 0, and D u in the readout uses u'.
+ *
+ * Workspace: the same size as selscan_fwd (selscan_fwd_workspace_bytes).
+ * Errors as selscan_fwd, and: SELSCAN_ERR_UNSUPPORTED for an unknown flag bit
+ * or conv_width > SELSCAN_MAX_CONV_WIDTH, SELSCAN_ERR_SHAPE for conv_width < 0,
+ * SELSCAN_ERR_NULL for conv_width > 0 without conv_weight.  conv_weight and
+ * conv_bias are inputs: they must not overlap y or h_last.
+ * The SELSCAN_FORCE_PLAN ablation does not apply to this call.
+ */
+int selscan_fwd_ex(const void *u, const void *delta, const float *A,
+                   const void *Bm, const void *Cm, const float *D_skip,
+                   const void *z, const float *delta_bias, int delta_softplus,
+                   const float *h0, void *y, float *h_last,
+                   int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
+                   int flags, const float *conv_weight, const float *conv_bias,
+                   int64_t conv_width,
+                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step, updating `state` in place:

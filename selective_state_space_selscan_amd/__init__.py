@@ -7,15 +7,21 @@ is no CPU fallback.  If ``libselscan.so`` is missing, every call raises.
 
     y = selscan_fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias)
     y, h_last = selscan_fwd(..., return_last_state=True)
+    y = selscan_fwd_ex(..., flags=SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_ZOH_EXACT,
+                       conv_weight=w, conv_bias=b)
     y = selscan_state_update(state, u, delta, A, Bm, Cm, D_skip, z, delta_bias)
 """
 from ._abi import (  # noqa: F401
     SELSCAN_BF16,
     SELSCAN_F32,
+    SELSCAN_FLAG_REVERSE,
+    SELSCAN_FLAG_ZOH_EXACT,
+    SELSCAN_MAX_CONV_WIDTH,
     SelscanError,
     lib,
     lib_path,
     selscan_fwd,
+    selscan_fwd_ex,
     selscan_fwd_workspace_bytes,
     selscan_state_update,
     status_string,

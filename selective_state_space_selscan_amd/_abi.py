@@ -14,6 +14,9 @@ import torch
 
 SELSCAN_F32 = 0
 SELSCAN_BF16 = 1
+SELSCAN_FLAG_ZOH_EXACT = 1
+SELSCAN_FLAG_REVERSE = 2
+SELSCAN_MAX_CONV_WIDTH = 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libselscan.so")
@@ -56,6 +59,9 @@ def lib():
         L.selscan_fwd.restype = I
         L.selscan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I,
                                   P, ctypes.c_size_t, P]
+        L.selscan_fwd_ex.restype = I
+        L.selscan_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I,
+                                     I, P, P, I64, P, ctypes.c_size_t, P]
         L.selscan_state_update.restype = I
         L.selscan_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
         _lib = L
@@ -116,6 +122,31 @@ def selscan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch
     u, delta, z: (batch, L, dim); Bm, Cm: (batch, L, N) in float32 or bfloat16;
     A: (dim, N), D_skip, delta_bias: (dim,), h0: (batch, dim, N) in float32.
     Returns y, or (y, h_last) when ``return_last_state``."""
+    return _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0,
+                return_last_state, y, h_last, workspace, stream, None)
+
+
+def selscan_fwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                   Cm: torch.Tensor, D_skip: Optional[torch.Tensor] = None,
+                   z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                   delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                   return_last_state: bool = False, flags: int = 0,
+                   conv_weight: Optional[torch.Tensor] = None,
+                   conv_bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                   h_last: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None):
+    """Forward with variants through ``selscan_fwd_ex``: ``flags`` is an OR of
+    SELSCAN_FLAG_ZOH_EXACT and SELSCAN_FLAG_REVERSE; ``conv_weight`` (dim, k)
+    float32 with k <= 4 (and ``conv_bias`` (dim,)) enables the causal conv1d +
+    SiLU prologue on u.  Other arguments and the result as ``selscan_fwd``."""
+    return _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0,
+                return_last_state, y, h_last, workspace, stream,
+                (int(flags), conv_weight, conv_bias))
+
+
+def _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, return_last_state, y,
+         h_last, workspace, stream, ex):
     L_ = lib()
     dev = u.device
     dt = u.dtype
@@ -142,14 +173,30 @@ def selscan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch
     ws_bytes = int(L_.selscan_fwd_workspace_bytes(batch, L, dim, N, code))
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    rc = L_.selscan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
-                        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(y),
-                        _ptr(h_last), batch, L, dim, N, code,
-                        _ptr(workspace) if ws_bytes else None,
-                        workspace.numel() * workspace.element_size() if ws_bytes else 0,
-                        _stream(dev, stream))
+    ws_ptr = _ptr(workspace) if ws_bytes else None
+    ws_len = workspace.numel() * workspace.element_size() if ws_bytes else 0
+    common = (_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
+              _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_last),
+              batch, L, dim, N, code)
+    if ex is None:
+        name = "selscan_fwd"
+        rc = L_.selscan_fwd(*common, ws_ptr, ws_len, _stream(dev, stream))
+    else:
+        name = "selscan_fwd_ex"
+        flags, conv_weight, conv_bias = ex
+        k = 0
+        if conv_weight is not None:
+            if conv_weight.dim() != 2:
+                raise ValueError("conv_weight must be (dim, k), got %s" % (tuple(conv_weight.shape),))
+            k = conv_weight.shape[1]
+            conv_weight = _prep(conv_weight, torch.float32, dev, "conv_weight", (dim, k))
+            conv_bias = _prep(conv_bias, torch.float32, dev, "conv_bias", (dim,))
+        elif conv_bias is not None:
+            raise ValueError("conv_bias given without conv_weight")
+        rc = L_.selscan_fwd_ex(*common, flags, _ptr(conv_weight), _ptr(conv_bias), k, ws_ptr,
+                               ws_len, _stream(dev, stream))
     if rc != 0:
-        raise SelscanError(rc, "selscan_fwd", L_.selscan_last_hip_error())
+        raise SelscanError(rc, name, L_.selscan_last_hip_error())
     return (y, h_last) if return_last_state else y
 
 

@@ -1,0 +1,657 @@
+// Streaming selective-scan forward for gfx950: kernel templates shared by the
+// default instantiation (fwd_stream.hip) and the variant instantiations
+// (fwd_stream_ext_n*.hip).
+//
+// What it computes is the S6 recurrence of the Mamba tutorial (pwwt.cn)
+// §3.1-§3.2 and §4.2: Delta_t = softplus(Delta_raw + bias), A_bar = exp(Delta_t A)
+// with diagonal A, h_t = A_bar_t h_{t-1} + Delta_t B_t u_t, y_t = C_t.h_t + D u_t,
+// times SiLU(z_t).  Discretisation, recurrence and readout run fused in one
+// kernel with the state in registers (tutorial §3.2, Gu & Dao deep-reading
+// report §2.4); only y (and h_L if asked) reaches HBM.
+//
+// Work decomposition: every wavefront is independent (no barriers, no LDS).
+//   * lane = one channel d of a 64-channel group of one batch row, so the
+//     u/Delta/z/y accesses of a wave are one contiguous row per timestep and
+//     B_t, C_t are wave-uniform: scalar loads into SGPRs, used directly as
+//     VALU operands.
+//   * wave = one (channel group, sequence part).  It walks its part of the
+//     sequence step by step with the N-entry state of each lane in VGPRs:
+//     per (t, n) one multiply for A_bar (see below), one for Delta B u, one FMA
+//     for the state and one FMA for the readout.
+//   * inputs of the next TT steps are loaded while the current TT are
+//     computed (two register buffers, no branch between them).
+// The sequence is split into P parts so that batch * dim / 64 * P waves fill
+// the chip.  A summary pass (SUMMARY = true) runs each part but the last from
+// a zero state and stores (sum of Delta over the part, end state); the main
+// pass starts part p from h0 folded through the summaries of parts 0..p-1
+// with the associative operator (a, b) o (c, d) = (a c, a d + b) of the
+// selection-mechanism article (discosf.com) §3.1, where the decay of a whole
+// part is exp(A sum Delta).
+//
+// Structured A: when every A[d, n] equals (n+1) A[d, 0] exactly (the S4D-real
+// initialisation A = -exp(log(1..N)) of the tutorial's §4.2 listing),
+// exp(Delta A[d, n]) = r^(n+1) with r = exp(Delta A[d, 0]), one multiply per
+// (t, n) instead of a multiply and an exp2.  A wave uses it only if all its
+// channels qualify; any other A takes the exp2 path.
+//
+// Variants (VAR has kVarExt set; the default instantiation VAR = 0 compiles
+// none of this):
+//   * reverse direction (runtime flag): the scan runs over the time-reversed
+//     sequence, t = L-1 down to 0 (the bidirectional use named in the
+//     tutorial's §7 outlook).  Parts, summaries and the fold are unchanged in
+//     scan order; only the scalar addressing maps scan step s to t = L-1-s.
+//   * exact zero-order hold (kVarZoh): B_bar = (exp(Delta A) - 1) / A * B
+//     (tutorial §2.2; selection-mechanism article §2.1) in place of Delta B.
+//   * causal depthwise conv1d + SiLU prologue (kVarConv): the scan input is
+//     u_s = SiLU(conv_bias + sum_j w_j x_{s-k+1+j}) over the raw input x, with
+//     x = 0 before the first step (tutorial §3.3 and its §4.2 listing: a
+//     grouped Conv1d with padding k-1 cut to the first L outputs, then SiLU).
+//     The last k-1 inputs ride along in registers.
+#pragma once
+
+#include "buffer_io.hpp"
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace selscan {
+namespace stream {
+
+constexpr int kLanes = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int TT = 4;   // timesteps per prefetch buffer, main pass
+constexpr int TTS = 8;  // timesteps per prefetch buffer, summary pass
+// A store offset past the byte range of every output descriptor (a chunk's
+// range is at most TT * dim * 4 bytes, and dim * 4 < 2^26 is checked on the
+// host), so stores from lanes past dim are dropped by the hardware.
+constexpr int kStoreOffsetOutOfRange = 1 << 30;
+static_assert(TT <= kStreamTT, "plan rounds parts to kStreamTT steps");
+
+enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4 };
+constexpr int kMaxConv = 4;
+
+// Variant arguments of the kernel (ignored when VAR = 0).
+struct ExtParams {
+    const float *conv_w;   // (dim, conv_k), or null
+    const float *conv_b;   // (dim), or null
+    int conv_k;
+    int rev;
+};
+
+template <int TTc>
+struct ChunkT {
+    uint32_t u[TTc], x[TTc], z[TTc];   // raw element bits, widened at use
+};
+using Chunk = ChunkT<TT>;
+
+struct WaveCtx {
+    int64_t b, d0, L, dim, l_begin, l_end;   // l_begin, l_end: part, in scan steps
+    int64_t bL;        // b * L: row of timestep 0 of this batch row
+    int voff, row_bytes;
+    int voff_store;    // voff, or an offset past every descriptor range for lanes past dim
+    float bias, Dd, A2_0;
+    int rev;           // variants: 1 = scan step s is timestep L-1-s
+    int softplus;      // variants: Delta = softplus(Delta_raw + bias) (else the sum)
+    float invA0;       // exact ZOH: 1 / A[d, 0]
+    float cw[kMaxConv], cb;   // conv prologue: taps (zero-padded in front), bias
+};
+
+// Row b*L + t of the (batch, L, .) arrays for scan step s.
+template <int VAR>
+__device__ __forceinline__ int64_t scan_row(const WaveCtx &c, int64_t s)
+{
+    if constexpr ((VAR & kVarExt) != 0)
+        return c.bL + (c.rev ? c.L - 1 - s : s);
+    else
+        return c.bL + s;
+}
+
+// Row step between consecutive scan steps: +1, or -1 in reverse direction.
+template <int VAR>
+__device__ __forceinline__ int64_t row_dir(const WaveCtx &c)
+{
+    if constexpr ((VAR & kVarExt) != 0)
+        return c.rev ? -1 : 1;
+    else
+        return 1;
+}
+
+// A run of `rows` consecutive scan steps starting at s0 occupies the
+// timesteps [t_lo, t_lo + rows).  Step i of the run sits at scalar offset
+// step_soff(...) from the element (t_lo, d0); steps at or past `rows` get an
+// offset past the descriptor range (reverse direction), or lie past it anyway.
+template <int VAR>
+__device__ __forceinline__ int64_t run_t_lo(const WaveCtx &c, int64_t s0, int64_t rows)
+{
+    if constexpr ((VAR & kVarExt) != 0)
+        return c.rev ? c.L - s0 - rows : s0;
+    else
+        return s0;
+}
+template <int VAR>
+__device__ __forceinline__ int step_soff(const WaveCtx &c, int i, int rows)
+{
+    if constexpr ((VAR & kVarExt) != 0) {
+        if (c.rev)
+            return i < rows ? (rows - 1 - i) * c.row_bytes : kStoreOffsetOutOfRange;
+    }
+    return i * c.row_bytes;
+}
+
+// Raw dwords of one B_t or C_t row (N values, two bf16 or one fp32 per dword).
+template <int N, typename TIO>
+struct RowRaw {
+    static constexpr int W = N * (int)sizeof(TIO) / 4;
+    uint32_t w[W];
+};
+
+template <int N, typename TIO>
+__device__ __forceinline__ void fetch_row(RowRaw<N, TIO> &r, const TIO *p, int64_t row)
+{
+    const const_u32 *q = as_const_u32(p) + row * RowRaw<N, TIO>::W;
+#pragma unroll
+    for (int k = 0; k < RowRaw<N, TIO>::W; ++k)
+        r.w[k] = q[k];
+}
+
+template <int N>
+__device__ __forceinline__ float row_val(const RowRaw<N, float> &r, int n)
+{
+    return __uint_as_float(r.w[n]);
+}
+template <int N>
+__device__ __forceinline__ float row_val(const RowRaw<N, uint16_t> &r, int n)
+{
+    const uint32_t w = r.w[n >> 1];
+    return __uint_as_float((n & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+template <bool GATED, int VAR, int TTc, typename TIO>
+__device__ __forceinline__ void load_chunk(ChunkT<TTc> &ch, const TIO *u, const TIO *delta,
+                                           const TIO *z, const WaveCtx &c, int64_t t0)
+{
+    constexpr int TT = TTc;
+    int64_t rows = c.l_end - t0;
+    rows = rows < 0 ? 0 : (rows > TT ? TT : rows);
+    if (t0 < c.l_begin)
+        rows = 0;
+    const int64_t elem = (c.bL + run_t_lo<VAR>(c, t0, rows)) * c.dim + c.d0;
+    // A chunk outside the part has an empty range: its loads return 0 and
+    // read nothing (the prefetch runs one chunk past either end).
+    const int64_t bytes = rows > 0 ? (rows * c.dim - c.d0) * (int64_t)sizeof(TIO) : 0;
+    const int64_t safe_elem = rows > 0 ? elem : 0;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + safe_elem, bytes);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(u + safe_elem, bytes);
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+        ch.x[i] = buf_load_raw(rd, c.voff, step_soff<VAR>(c, i, (int)rows), delta);
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+        ch.u[i] = buf_load_raw(ru, c.voff, step_soff<VAR>(c, i, (int)rows), u);
+    if (GATED) {
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(z + safe_elem, bytes);
+#pragma unroll
+        for (int i = 0; i < TT; ++i)
+            ch.z[i] = buf_load_raw(rz, c.voff, step_soff<VAR>(c, i, (int)rows), z);
+    }
+}
+
+// Scan input of one step: the loaded value, or with the conv prologue the
+// causal conv over the last kMaxConv raw inputs, then SiLU.  win holds the
+// kMaxConv - 1 raw inputs before this step, oldest first.
+template <int VAR, typename TIO>
+__device__ __forceinline__ float step_input(uint32_t raw, const WaveCtx &c,
+                                            float (&win)[kMaxConv - 1])
+{
+    const float x = raw_to_f32(raw, tag<TIO>());
+    if constexpr ((VAR & kVarConv) != 0) {
+        float acc = c.cb;
+#pragma unroll
+        for (int j = 0; j < kMaxConv - 1; ++j)
+            acc = fmaf(c.cw[j], win[j], acc);
+        acc = fmaf(c.cw[kMaxConv - 1], x, acc);
+#pragma unroll
+        for (int j = 0; j < kMaxConv - 2; ++j)
+            win[j] = win[j + 1];
+        win[kMaxConv - 2] = x;
+        return silu(acc);
+    } else {
+        return x;
+    }
+}
+
+// Delta of one step.  The default instantiation has the softplus switch as a
+// template argument; the variants select at run time (one instantiation less).
+template <bool SOFTPLUS, int VAR>
+__device__ __forceinline__ float step_delta(float x, const WaveCtx &c)
+{
+    if constexpr ((VAR & kVarExt) != 0) {
+        const float sp = softplus(x);
+        return c.softplus ? sp : x;
+    } else {
+        return SOFTPLUS ? softplus(x) : x;
+    }
+}
+
+// Exact zero-order-hold coefficient (exp(Delta a) - 1) / a, given
+// x2 = Delta a log2(e) and e = 2^x2 = exp(Delta a).  Where |Delta a| is
+// small, e - 1 cancels, so the Taylor series of Delta * (e^x - 1) / x in
+// x = Delta a (degree 4, truncation below 1e-8 relative for |x2| < 1/8) is
+// used there; elsewhere the cancellation costs at most 1 ulp(e) / |e - 1|,
+// below 1e-6 relative.  a = 0 gives x2 = 0 and the series value Delta.
+__device__ __forceinline__ float zoh_coeff(float dt, float x2, float e, float inv_a)
+{
+    constexpr float k1 = kLn2 / 2.0f;
+    constexpr float k2 = kLn2 * kLn2 / 6.0f;
+    constexpr float k3 = kLn2 * kLn2 * kLn2 / 24.0f;
+    constexpr float k4 = kLn2 * kLn2 * kLn2 * kLn2 / 120.0f;
+    const float series = dt * fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, k4, k3), k2), k1), 1.0f);
+    const float direct = (e - 1.0f) * inv_a;
+    return fabsf(x2) < 0.125f ? series : direct;
+}
+
+// TT steps of the recurrence on one prefetched chunk.  FULL: all TT steps are
+// inside the range (no per-step check); otherwise steps past the end are the
+// identity element (Delta = 0).  The B_t / C_t rows of step i+1 are fetched
+// (scalar loads) while step i computes.  The loop body has no branch, so the
+// scheduler is free to move loads ahead.
+template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, bool FULL, int VAR,
+          typename TIO>
+__device__ __forceinline__ void run_chunk(const Chunk &ch, const TIO *Bm, const TIO *Cm, TIO *y,
+                                          const WaveCtx &c, int64_t t0, const float (&A2)[N],
+                                          const float (&invA)[N], float (&h)[N], float &sdelta,
+                                          float (&win)[kMaxConv - 1])
+{
+    constexpr bool ZOH = (VAR & kVarZoh) != 0;
+    const int rows = FULL ? TT : (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
+    const int64_t elem = (c.bL + run_t_lo<VAR>(c, t0, rows)) * c.dim + c.d0;
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(SUMMARY ? nullptr : y + elem, SUMMARY ? 0 : (rows * c.dim - c.d0) * (int64_t)sizeof(TIO));
+    const int64_t row0 = scan_row<VAR>(c, t0);
+    const int64_t row_last = scan_row<VAR>(c, c.L - 1);
+    const int64_t dir = row_dir<VAR>(c);
+    RowRaw<N, TIO> bcur, ccur, bnxt, cnxt;
+    fetch_row(bcur, Bm, row0);
+    if (!SUMMARY)
+        fetch_row(ccur, Cm, row0);
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        if (i + 1 < TT) {
+            // steps past L read the last row (padding steps, never stored)
+            const int64_t rn = (FULL || t0 + i + 1 <= c.L - 1) ? row0 + (i + 1) * dir : row_last;
+            fetch_row(bnxt, Bm, rn);
+            if (!SUMMARY)
+                fetch_row(cnxt, Cm, rn);
+        }
+        const bool valid = FULL || i < rows;
+        const float ut = step_input<VAR, TIO>(ch.u[i], c, win);
+        const float x = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
+        float dt = step_delta<SOFTPLUS, VAR>(x, c);
+        if (!FULL)
+            dt = valid ? dt : 0.0f;        // padding steps are the identity (1, 0)
+        const float du = dt * ut;
+        float yv = c.Dd * ut;
+        const float r = POW ? hw_exp2(dt * c.A2_0) : 0.0f;
+        float pw = 1.0f;
+        // exact ZOH with structured A: r^(n+1) - 1 = (r - 1)(1 + r + ... + r^n),
+        // so B_bar_n / B_n = em * S_n / (n+1) with em = (r - 1) / A[d,0] and
+        // S_n = 1 + r + ... + r^n (a running sum of the powers).
+        const float g = (ZOH && POW) ? zoh_coeff(dt, dt * c.A2_0, r, c.invA0) * ut : 0.0f;
+        float S = 1.0f;
+        if (SUMMARY)
+            sdelta += dt;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            float a, bu;
+            if constexpr (ZOH) {
+                if (POW) {
+                    a = (pw *= r);
+                    bu = (g * (1.0f / (float)(n + 1))) * (S * row_val<N>(bcur, n));
+                    S += a;
+                } else {
+                    const float x2 = dt * A2[n];
+                    a = hw_exp2(x2);
+                    bu = zoh_coeff(dt, x2, a, invA[n]) * (ut * row_val<N>(bcur, n));
+                }
+            } else {
+                a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
+                bu = du * row_val<N>(bcur, n);
+            }
+            h[n] = fmaf(a, h[n], bu);
+            if (!SUMMARY)
+                yv = fmaf(row_val<N>(ccur, n), h[n], yv);
+        }
+        if (!SUMMARY) {
+            if (GATED)
+                yv *= silu(raw_to_f32(ch.z[i], tag<TIO>()));
+            // rows past the end and lanes past dim fall outside the descriptor
+            buf_store(ry, c.voff_store, step_soff<VAR>(c, i, rows), yv, y);
+        }
+        if (i + 1 < TT) {
+            bcur = bnxt;
+            if (!SUMMARY)
+                ccur = cnxt;
+        }
+    }
+}
+
+template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, int VAR, typename TIO>
+__device__ __forceinline__ void run_any_chunk(const Chunk &ch, const TIO *Bm, const TIO *Cm, TIO *y,
+                                              const WaveCtx &c, int64_t t0,
+                                              const float (&A2)[N], const float (&invA)[N],
+                                              float (&h)[N], float &sdelta,
+                                              float (&win)[kMaxConv - 1])
+{
+    if (t0 + TT <= c.l_end)
+        run_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, true, VAR>(ch, Bm, Cm, y, c, t0, A2, invA, h,
+                                                               sdelta, win);
+    else
+        run_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, false, VAR>(ch, Bm, Cm, y, c, t0, A2, invA, h,
+                                                                sdelta, win);
+}
+
+// Forward walk over the part (main pass, and the summary for general A).
+template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, int VAR, typename TIO>
+__device__ __forceinline__ void run_part(const TIO *u, const TIO *delta, const TIO *z, TIO *y,
+                                         const TIO *Bm, const TIO *Cm, const WaveCtx &c,
+                                         const float (&A2)[N], const float (&invA)[N],
+                                         float (&h)[N], float &sdelta, float (&win)[kMaxConv - 1])
+{
+    Chunk A, B;
+    int64_t t0 = c.l_begin;
+    load_chunk<GATED, VAR>(A, u, delta, z, c, t0);
+    for (;;) {
+        load_chunk<GATED, VAR>(B, u, delta, z, c, t0 + TT);
+        run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, VAR>(A, Bm, Cm, y, c, t0, A2, invA, h,
+                                                             sdelta, win);
+        t0 += TT;
+        if (t0 >= c.l_end)
+            break;
+        load_chunk<GATED, VAR>(A, u, delta, z, c, t0 + TT);
+        run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, VAR>(B, Bm, Cm, y, c, t0, A2, invA, h,
+                                                             sdelta, win);
+        t0 += TT;
+        if (t0 >= c.l_end)
+            break;
+    }
+}
+
+// Summary of a part for structured A, walking the part backwards in time.
+// The end state from zero is x[n] = sum_t Q_t^(n+1) Delta_t u_t B_t[n], with
+// Q_t = prod_{s>t} r_s and r_s = exp(Delta_s A[d,0]).  Walking backwards, Q
+// is one running product and Delta_t u_t Q_t^(n+1) one multiply per n, so a
+// (t, n) costs a multiply and an FMA (the forward walk needs three ops).
+// Not used with the exact-ZOH or conv variants (their input of a step is
+// not Delta_t u_t, or depends on the steps before it).
+template <int N, bool SOFTPLUS, bool FULL, int VAR, typename TIO>
+__device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const TIO *Bm,
+                                                  const WaveCtx &c, int64_t t0, float &Q,
+                                                  float (&x)[N], float &sdelta)
+{
+    constexpr int TT = TTS;
+    const int rows = FULL ? TT : (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
+    // B_t row of step i-1 is fetched (scalar loads) while step i computes.
+    const int64_t row0 = scan_row<VAR>(c, t0);
+    const int64_t dir = row_dir<VAR>(c);
+    RowRaw<N, TIO> bcur, bnxt;
+    fetch_row(bcur, Bm, row0 + (FULL ? TT - 1 : rows - 1) * dir);
+#pragma unroll
+    for (int i = TT - 1; i >= 0; --i) {
+        if (!FULL && i >= rows)
+            continue;   // uniform: steps past the end contribute nothing
+        if (i > 0)
+            fetch_row(bnxt, Bm, row0 + (i - 1) * dir);
+        const float ut = raw_to_f32(ch.u[i], tag<TIO>());
+        const float xr = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
+        const float dt = step_delta<SOFTPLUS, VAR>(xr, c);
+        sdelta += dt;
+        float g = dt * ut * Q;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            if (n)
+                g *= Q;
+            x[n] = fmaf(g, row_val<N>(bcur, n), x[n]);
+        }
+        Q *= hw_exp2(dt * c.A2_0);
+        if (i > 0)
+            bcur = bnxt;
+    }
+}
+
+template <int N, bool SOFTPLUS, int VAR, typename TIO>
+__device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta, const TIO *Bm,
+                                                 const WaveCtx &c, float (&x)[N], float &sdelta)
+{
+    constexpr int TT = TTS;
+    const int64_t nchunks = (c.l_end - c.l_begin + TT - 1) / TT;
+    ChunkT<TTS> A, B;
+    float Q = 1.0f;
+    int64_t k = nchunks - 1;
+    int64_t t0 = c.l_begin + k * TT;
+    load_chunk<false, VAR>(A, u, delta, (const TIO *)nullptr, c, t0);
+    // the last chunk may be partial; every other chunk is full
+    load_chunk<false, VAR>(B, u, delta, (const TIO *)nullptr, c, t0 - TT);
+    if (t0 + TT <= c.l_end)
+        summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, Bm, c, t0, Q, x, sdelta);
+    else
+        summary_chunk_rev<N, SOFTPLUS, false, VAR>(A, Bm, c, t0, Q, x, sdelta);
+    for (;;) {
+        if (--k < 0)
+            break;
+        t0 -= TT;
+        load_chunk<false, VAR>(A, u, delta, (const TIO *)nullptr, c, t0 - TT);
+        summary_chunk_rev<N, SOFTPLUS, true, VAR>(B, Bm, c, t0, Q, x, sdelta);
+        if (--k < 0)
+            break;
+        t0 -= TT;
+        load_chunk<false, VAR>(B, u, delta, (const TIO *)nullptr, c, t0 - TT);
+        summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, Bm, c, t0, Q, x, sdelta);
+    }
+}
+
+// Occupancy target: four waves per SIMD (at most 128 VGPRs) for N <= 16;
+// three (at most 168 VGPRs) for the exact-ZOH and conv variants, whose
+// coefficients and taps would spill at 128.
+template <int N, int VAR>
+constexpr int waves_per_eu()
+{
+    if (N > 16)
+        return 1;
+    return (VAR & (kVarZoh | kVarConv)) != 0 ? 3 : 4;
+}
+
+template <int N, bool SUMMARY, int VAR, typename TIO>
+__global__ __launch_bounds__(kLanes * kWavesPerBlock)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_kernel(
+    const TIO *__restrict__ u, const TIO *__restrict__ delta, const TIO *__restrict__ z,
+    TIO *__restrict__ y, const float *__restrict__ A, const TIO *__restrict__ Bm,
+    const TIO *__restrict__ Cm, const float *__restrict__ D_skip,
+    const float *__restrict__ delta_bias, int delta_softplus, const float *__restrict__ h0,
+    float *__restrict__ h_last, float *__restrict__ summ, int64_t L, int64_t dim,
+    int64_t groups, int parts, int64_t part_len, ExtParams ext)
+{
+    constexpr bool EXT = (VAR & kVarExt) != 0;
+    constexpr bool ZOH = (VAR & kVarZoh) != 0;
+    constexpr bool CONV = (VAR & kVarConv) != 0;
+    const int lane = threadIdx.x & (kLanes - 1);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves_parts = SUMMARY ? parts - 1 : parts;
+    if (gw >= groups * waves_parts)
+        return;   // whole wave: waves never synchronise with each other
+    const int part = (int)(gw / groups);
+    const int64_t grp = gw % groups;
+    const int64_t groups_per_row = (dim + kLanes - 1) / kLanes;
+
+    WaveCtx c;
+    c.b = grp / groups_per_row;
+    c.bL = c.b * L;
+    c.d0 = (grp % groups_per_row) * kLanes;
+    c.L = L;
+    c.dim = dim;
+    c.l_begin = (int64_t)part * part_len;
+    c.l_end = c.l_begin + part_len < L ? c.l_begin + part_len : L;
+    c.voff = lane * (int)sizeof(TIO);
+    c.row_bytes = (int)(dim * (int64_t)sizeof(TIO));
+    const bool active = c.d0 + lane < dim;
+    const int64_t d = active ? c.d0 + lane : dim - 1;
+    c.voff_store = active ? c.voff : kStoreOffsetOutOfRange;
+    c.rev = EXT ? ext.rev : 0;
+    c.softplus = delta_softplus;
+
+    const float A0 = A[d * N];
+    bool structured = true;
+    float A2[N], invA[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float an = A[d * N + n];
+        A2[n] = an * kLog2e;
+        invA[n] = ZOH ? 1.0f / an : 0.0f;
+        structured = structured && (an == (float)(n + 1) * A0);
+    }
+    const bool pow_path = __all(structured);
+    c.A2_0 = A0 * kLog2e;
+    c.invA0 = invA[0];
+    c.bias = delta_bias ? delta_bias[d] : 0.0f;
+    c.Dd = (!SUMMARY && D_skip) ? D_skip[d] : 0.0f;
+
+    // Conv prologue: taps aligned to the newest input (zeros in front when
+    // conv_k < kMaxConv), and the raw inputs of the steps before the part.
+    float win[kMaxConv - 1];
+#pragma unroll
+    for (int j = 0; j < kMaxConv - 1; ++j)
+        win[j] = 0.0f;
+    if constexpr (CONV) {
+#pragma unroll
+        for (int m = 0; m < kMaxConv; ++m) {
+            const int j = m - (kMaxConv - ext.conv_k);
+            c.cw[m] = j >= 0 ? ext.conv_w[d * ext.conv_k + j] : 0.0f;
+        }
+        c.cb = ext.conv_b ? ext.conv_b[d] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxConv - 1; ++j) {
+            const int64_t s = c.l_begin - (kMaxConv - 1) + j;
+            if (s >= 0)
+                win[j] = load_elem(u, scan_row<VAR>(c, s) * dim + d);
+        }
+    }
+
+    // Entry state: zero for a summary; for the main pass h0 (or zero) carried
+    // through the summaries of the parts before this one.
+    float h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+        h[n] = (!SUMMARY && h0) ? h0[(c.b * dim + d) * N + n] : 0.0f;
+    if (!SUMMARY) {
+        // h <- exp(A S) h + x for each earlier part (S = its sum of Delta, x =
+        // its end state from zero); for structured A, exp(A[d,n] S) = e^(n+1).
+        for (int q = 0; q < part; ++q) {
+            const float *s = summ + ((grp * (parts - 1) + q) * (N + 1)) * kLanes + lane;
+            const float S = s[0];
+            if (pow_path) {
+                const float e = hw_exp2(c.A2_0 * S);
+                float pw = 1.0f;
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    pw *= e;
+                    h[n] = fmaf(pw, h[n], s[(n + 1) * kLanes]);
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    h[n] = fmaf(hw_exp2(A2[n] * S), h[n], s[(n + 1) * kLanes]);
+            }
+        }
+    }
+
+    float sdelta = 0.0f;
+    const bool gated = !SUMMARY && z != nullptr;
+#define SELSCAN_RUN(G, SP, PW)                                                                    \
+    run_part<N, SUMMARY, G, SP, PW, VAR>(u, delta, z, y, Bm, Cm, c, A2, invA, h, sdelta, win)
+    if (SUMMARY && pow_path && !ZOH && !CONV) {
+        if (EXT || delta_softplus)
+            summary_part_rev<N, true, VAR>(u, delta, Bm, c, h, sdelta);
+        else
+            summary_part_rev<N, false, VAR>(u, delta, Bm, c, h, sdelta);
+    } else if (gated) {
+        if (EXT || delta_softplus) {
+            if (pow_path) SELSCAN_RUN(true, true, true); else SELSCAN_RUN(true, true, false);
+        } else {
+            if (pow_path) SELSCAN_RUN(true, false, true); else SELSCAN_RUN(true, false, false);
+        }
+    } else {
+        if (EXT || delta_softplus) {
+            if (pow_path) SELSCAN_RUN(false, true, true); else SELSCAN_RUN(false, true, false);
+        } else {
+            if (pow_path) SELSCAN_RUN(false, false, true); else SELSCAN_RUN(false, false, false);
+        }
+    }
+#undef SELSCAN_RUN
+
+    if (SUMMARY) {
+        float *o = summ + ((grp * (parts - 1) + part) * (N + 1)) * kLanes + lane;
+        o[0] = sdelta;
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            o[(n + 1) * kLanes] = h[n];
+    } else if (h_last && active && part == parts - 1) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            h_last[(c.b * dim + d) * N + n] = h[n];
+    }
+}
+
+// Summary pass (when the sequence is split), then the main pass, on one stream.
+template <int N, int VAR, typename TIO>
+hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p, float *summ,
+                    hipStream_t s)
+{
+    if (p.parts > 1) {
+        const int64_t waves = p.groups * (p.parts - 1);
+        hipLaunchKernelGGL((fwd_stream_kernel<N, true, VAR, TIO>),
+                           dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                           dim3(kLanes * kWavesPerBlock), 0, s, (const TIO *)a.u,
+                           (const TIO *)a.delta, (const TIO *)nullptr, (TIO *)nullptr, a.A,
+                           (const TIO *)a.Bm, (const TIO *)a.Cm, (const float *)nullptr,
+                           a.delta_bias, a.delta_softplus, (const float *)nullptr,
+                           (float *)nullptr, summ, a.L, a.dim, p.groups, p.parts, p.part_len, ext);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t waves = p.groups * p.parts;
+    hipLaunchKernelGGL((fwd_stream_kernel<N, false, VAR, TIO>),
+                       dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kLanes * kWavesPerBlock), 0, s, (const TIO *)a.u, (const TIO *)a.delta,
+                       (const TIO *)a.z, (TIO *)a.y, a.A, (const TIO *)a.Bm, (const TIO *)a.Cm,
+                       a.D_skip, a.delta_bias, a.delta_softplus, a.h0, a.h_last, summ, a.L,
+                       a.dim, p.groups, p.parts, p.part_len, ext);
+    return hipGetLastError();
+}
+
+inline float *summary_buffer(void *workspace)
+{
+    return (float *)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+}
+
+// Variant forward for one N and one B_bar form (ZOH: exact zero-order hold):
+// picks the instantiation from the conv width and the dtype.
+template <int N, bool ZOH>
+hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
+{
+    const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim);
+    float *summ = summary_buffer(a.workspace);
+    ExtParams x;
+    x.conv_w = e.conv_k > 0 ? e.conv_w : nullptr;
+    x.conv_b = e.conv_k > 0 ? e.conv_b : nullptr;
+    x.conv_k = e.conv_k;
+    x.rev = (e.flags & kFwdFlagReverse) ? 1 : 0;
+    constexpr int V = kVarExt | (ZOH ? kVarZoh : 0);
+    const bool bf = a.dtype == 1;
+    if (e.conv_k > 0)
+        return bf ? launch_n<N, V | kVarConv, uint16_t>(a, x, p, summ, s)
+                  : launch_n<N, V | kVarConv, float>(a, x, p, summ, s);
+    return bf ? launch_n<N, V, uint16_t>(a, x, p, summ, s) : launch_n<N, V, float>(a, x, p, summ, s);
+}
+
+} // namespace stream
+} // namespace selscan

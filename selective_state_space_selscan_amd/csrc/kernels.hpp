@@ -52,8 +52,36 @@ hipError_t launch_fwd_chunked(const FwdArgs &a, hipStream_t stream);
 
 // Streaming forward (default): independent waves over sequence parts, with a
 // summary pre-pass when the sequence is split.
+constexpr int kStreamTT = 4;   // part lengths are multiples of this many steps
+struct StreamPlan {
+    int64_t groups;     // batch * ceil(dim / 64) channel groups
+    int64_t part_len;   // steps per sequence part
+    int parts;
+};
+StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim);
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
+
+// Variants of the streaming forward (same plan and workspace).
+constexpr int kFwdFlagZohExact = 1;
+constexpr int kFwdFlagReverse = 2;
+struct FwdExt {
+    int flags;            // kFwdFlagZohExact | kFwdFlagReverse
+    const float *conv_w;  // (dim, conv_k) when conv_k > 0
+    const float *conv_b;  // (dim) or null
+    int conv_k;           // 0 = no conv prologue, else 1..4
+};
+hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream);
+// One translation unit per (N, B_bar form): fwd_stream_ext_n<N>[_zoh].hip.
+#define SELSCAN_DECLARE_EXT(NN)                                                                   \
+    hipError_t launch_fwd_stream_ext_n##NN(const FwdArgs &a, const FwdExt &e, hipStream_t s);    \
+    hipError_t launch_fwd_stream_ext_n##NN##_zoh(const FwdArgs &a, const FwdExt &e, hipStream_t s);
+SELSCAN_DECLARE_EXT(4)
+SELSCAN_DECLARE_EXT(8)
+SELSCAN_DECLARE_EXT(16)
+SELSCAN_DECLARE_EXT(32)
+SELSCAN_DECLARE_EXT(64)
+#undef SELSCAN_DECLARE_EXT
 
 // Decode step.
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);

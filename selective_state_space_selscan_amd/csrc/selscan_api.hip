@@ -80,6 +80,73 @@ int finish_launch(hipError_t e)
 
 } // namespace
 
+namespace {
+
+// Shared by selscan_fwd (ext == NULL) and selscan_fwd_ex.
+int fwd_common(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+               const float *D_skip, const void *z, const float *delta_bias, int delta_softplus,
+               const float *h0, void *y, float *h_last, int64_t batch, int64_t L, int64_t dim,
+               int64_t N, int dtype, const selscan::FwdExt *ext, void *workspace,
+               size_t workspace_bytes, void *stream)
+{
+    if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
+        return SELSCAN_ERR_DTYPE;
+    const int64_t elems = checked_count(batch, L, dim);
+    const int64_t bcn = checked_count(batch, L, N > 0 ? N : 1);
+    const int64_t states = checked_count(batch, dim, N > 0 ? N : 1);
+    if (elems < 0 || bcn < 0 || states < 0 || N < 1)
+        return SELSCAN_ERR_SHAPE;
+    if (!u || !delta || !A || !Bm || !Cm || !y)
+        return SELSCAN_ERR_NULL;
+    if (!supported_n(N) || dim > kMaxDim)
+        return SELSCAN_ERR_UNSUPPORTED;
+    const float *conv_w = ext && ext->conv_k > 0 ? ext->conv_w : nullptr;
+    const float *conv_b = ext && ext->conv_k > 0 ? ext->conv_b : nullptr;
+    const int64_t conv_k = ext ? ext->conv_k : 0;
+    if (ext && ext->conv_k > 0 && !conv_w)
+        return SELSCAN_ERR_NULL;
+    const void *all[] = {u, delta, A, Bm, Cm, D_skip, z, delta_bias, h0, y, h_last, workspace,
+                         conv_w, conv_b};
+    for (const void *p : all)
+        if (p && !aligned16(p))
+            return SELSCAN_ERR_UNSUPPORTED;
+    const size_t need = selscan_fwd_workspace_bytes(batch, L, dim, N, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return SELSCAN_ERR_WORKSPACE;
+
+    const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
+    const Range ins[] = {{u, elems * es},     {delta, elems * es},     {A, dim * N * 4},
+                         {Bm, bcn * es},      {Cm, bcn * es},          {D_skip, dim * 4},
+                         {z, elems * es},     {delta_bias, dim * 4},   {h0, states * 4},
+                         {workspace, (int64_t)need}, {conv_w, dim * conv_k * 4},
+                         {conv_b, dim * 4}};
+    const Range outs[] = {{y, elems * es}, {h_last, states * 4}};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return SELSCAN_ERR_ALIAS;
+    if (overlaps(outs[0], outs[1]))
+        return SELSCAN_ERR_ALIAS;
+
+    selscan::FwdArgs a;
+    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
+    a.delta_bias = delta_bias; a.delta_softplus = delta_softplus ? 1 : 0; a.h0 = h0; a.y = y;
+    a.h_last = h_last; a.batch = batch; a.L = L; a.dim = dim; a.N = N; a.dtype = dtype;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    if (ext)
+        return finish_launch(selscan::launch_fwd_stream_ext(a, *ext, (hipStream_t)stream));
+    switch (forced_plan()) {
+    case PLAN_SERIAL:
+        return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
+    case PLAN_CHUNKED:
+        return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
+    default:
+        return finish_launch(selscan::launch_fwd_stream(a, (hipStream_t)stream));
+    }
+}
+
+} // namespace
+
 extern "C" {
 
 int selscan_abi_version(void) { return SELSCAN_ABI_VERSION; }
@@ -118,51 +185,31 @@ int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm
                 const float *h0, void *y, float *h_last, int64_t batch, int64_t L, int64_t dim,
                 int64_t N, int dtype, void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
-        return SELSCAN_ERR_DTYPE;
-    const int64_t elems = checked_count(batch, L, dim);
-    const int64_t bcn = checked_count(batch, L, N > 0 ? N : 1);
-    const int64_t states = checked_count(batch, dim, N > 0 ? N : 1);
-    if (elems < 0 || bcn < 0 || states < 0 || N < 1)
-        return SELSCAN_ERR_SHAPE;
-    if (!u || !delta || !A || !Bm || !Cm || !y)
-        return SELSCAN_ERR_NULL;
-    if (!supported_n(N) || dim > kMaxDim)
+    return fwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, y, h_last,
+                      batch, L, dim, N, dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+int selscan_fwd_ex(const void *u, const void *delta, const float *A, const void *Bm,
+                   const void *Cm, const float *D_skip, const void *z, const float *delta_bias,
+                   int delta_softplus, const float *h0, void *y, float *h_last, int64_t batch,
+                   int64_t L, int64_t dim, int64_t N, int dtype, int flags,
+                   const float *conv_weight, const float *conv_bias, int64_t conv_width,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE))
         return SELSCAN_ERR_UNSUPPORTED;
-    const void *all[] = {u, delta, A, Bm, Cm, D_skip, z, delta_bias, h0, y, h_last, workspace};
-    for (const void *p : all)
-        if (p && !aligned16(p))
-            return SELSCAN_ERR_UNSUPPORTED;
-    const size_t need = selscan_fwd_workspace_bytes(batch, L, dim, N, dtype);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return SELSCAN_ERR_WORKSPACE;
-
-    const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
-    const Range ins[] = {{u, elems * es},     {delta, elems * es},     {A, dim * N * 4},
-                         {Bm, bcn * es},      {Cm, bcn * es},          {D_skip, dim * 4},
-                         {z, elems * es},     {delta_bias, dim * 4},   {h0, states * 4},
-                         {workspace, (int64_t)need}};
-    const Range outs[] = {{y, elems * es}, {h_last, states * 4}};
-    for (const Range &o : outs)
-        for (const Range &i : ins)
-            if (overlaps(o, i))
-                return SELSCAN_ERR_ALIAS;
-    if (overlaps(outs[0], outs[1]))
-        return SELSCAN_ERR_ALIAS;
-
-    selscan::FwdArgs a;
-    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
-    a.delta_bias = delta_bias; a.delta_softplus = delta_softplus ? 1 : 0; a.h0 = h0; a.y = y;
-    a.h_last = h_last; a.batch = batch; a.L = L; a.dim = dim; a.N = N; a.dtype = dtype;
-    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    switch (forced_plan()) {
-    case PLAN_SERIAL:
-        return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
-    case PLAN_CHUNKED:
-        return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
-    default:
-        return finish_launch(selscan::launch_fwd_stream(a, (hipStream_t)stream));
-    }
+    if (conv_width < 0)
+        return SELSCAN_ERR_SHAPE;
+    if (conv_width > SELSCAN_MAX_CONV_WIDTH)
+        return SELSCAN_ERR_UNSUPPORTED;
+    selscan::FwdExt e;
+    e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |
+              (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0);
+    e.conv_w = conv_weight;
+    e.conv_b = conv_bias;
+    e.conv_k = (int)conv_width;
+    return fwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, y, h_last,
+                      batch, L, dim, N, dtype, &e, workspace, workspace_bytes, stream);
 }
 
 int selscan_state_update(float *state, const void *u, const void *delta, const float *A,

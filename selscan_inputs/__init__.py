@@ -244,3 +244,13 @@ def decode_block(w: Workload, k0: int, k1: int, threads: int = 8):
     from concurrent.futures import ThreadPoolExecutor
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         return list(ex.map(lambda k: decode_step_inputs(w, k), range(k0, k1)))
+
+
+def conv_params(dim: int, k: int, seed: int, with_bias: bool = True):
+    """Depthwise causal conv taps (dim, k) and bias (dim,) in fp32, drawn
+    uniform in +-1/sqrt(k) (the fan-in bound of a default grouped Conv1d)."""
+    rng = np.random.default_rng([seed, 7919])
+    bound = 1.0 / np.sqrt(k)
+    w = rng.uniform(-bound, bound, size=(dim, k)).astype(np.float32)
+    b = rng.uniform(-bound, bound, size=dim).astype(np.float32) if with_bias else None
+    return w, b

@@ -43,7 +43,8 @@ def header_constant(name):
 def test_library_exports_every_declared_symbol():
     L = ss.lib()
     names = header_functions()
-    assert {"selscan_fwd", "selscan_state_update", "selscan_fwd_workspace_bytes"} <= set(names)
+    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_state_update",
+            "selscan_fwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), "missing export " + n
     assert L.selscan_abi_version() == header_constant("SELSCAN_ABI_VERSION")
@@ -127,6 +128,53 @@ def test_fwd_workspace_checked_when_needed():
     # misaligned workspace
     args = fwd_args(batch=1, L=131072, dim=2048, workspace=ctypes.c_void_p(BASE + 12 * STEP + 8))
     assert L.selscan_fwd(*args) == ERR_UNSUP
+
+
+def fwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, **kw):
+    a = fwd_args(**kw)
+    # flags, conv_weight, conv_bias, conv_width go between dtype and workspace
+    return a[:17] + [flags, conv_w, conv_b, conv_width] + a[17:]
+
+
+INVALID_FWD_EX = [
+    ("unknown_flag", dict(flags=4), ERR_UNSUP),
+    ("negative_flag", dict(flags=-1), ERR_UNSUP),
+    ("conv_width_5", dict(conv_width=5, conv_w=fake(13)), ERR_UNSUP),
+    ("conv_width_neg", dict(conv_width=-1, conv_w=fake(13)), ERR_SHAPE),
+    ("conv_w_null", dict(conv_width=4, conv_w=None), ERR_NULL),
+    ("conv_w_misaligned", dict(conv_width=4, conv_w=ctypes.c_void_p(BASE + 13 * STEP + 4)),
+     ERR_UNSUP),
+    ("conv_b_misaligned", dict(conv_width=4, conv_w=fake(13),
+                               conv_b=ctypes.c_void_p(BASE + 14 * STEP + 8)), ERR_UNSUP),
+    ("y_aliases_conv_w", dict(conv_width=4, conv_w=ctypes.c_void_p(BASE + 10 * STEP + 512)),
+     ERR_ALIAS),
+    ("hlast_aliases_conv_b", dict(conv_width=2, conv_w=fake(13),
+                                  conv_b=ctypes.c_void_p(BASE + 11 * STEP + 256)), ERR_ALIAS),
+    # the checks of selscan_fwd apply as well
+    ("dtype", dict(dtype=2, flags=1), ERR_DTYPE),
+    ("L0", dict(L=0, flags=2), ERR_SHAPE),
+    ("N5", dict(N=5, flags=3), ERR_UNSUP),
+    ("u_null", dict(u=None, conv_width=4, conv_w=fake(13)), ERR_NULL),
+    ("y_aliases_u", dict(y=ctypes.c_void_p(BASE + STEP + 64), flags=2), ERR_ALIAS),
+]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("name,kw,status", INVALID_FWD_EX, ids=[c[0] for c in INVALID_FWD_EX])
+def test_fwd_ex_rejects_invalid_arguments(name, kw, status):
+    L = ss.lib()
+    assert L.selscan_fwd_ex(*fwd_ex_args(**kw)) == status
+    assert L.selscan_last_hip_error() == 0
+
+
+@no_gpu_only
+def test_fwd_ex_workspace_checked_when_needed():
+    L = ss.lib()
+    need = L.selscan_fwd_workspace_bytes(1, 131072, 2048, 16, 1)
+    for ws, nbytes in ((None, 0), (fake(12), need - 1)):
+        args = fwd_ex_args(flags=3, conv_width=4, conv_w=fake(13), batch=1, L=131072, dim=2048,
+                           workspace=ws, workspace_bytes=nbytes)
+        assert L.selscan_fwd_ex(*args) == ERR_WS
 
 
 def step_args(**kw):
