@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 ``selscan_oracle.c`` is the sequential fp64 definition of the scan (see its
 header for the page citations).  ``build()`` compiles it with gcc + OpenMP;
-``fwd`` and ``state_update`` wrap it for numpy arrays.
+``fwd``, ``bwd`` and ``state_update`` wrap it for numpy arrays.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (LTI convolution, closed-form double sum, associative scan, Delta limits,
@@ -13,7 +13,9 @@ softplus round trip, skip path, split invariance, decode = forward,
 causality, permutation and linearity); the variants of ``fwd`` by the LTI
 convolution with the exact zero-order-hold kernel, its A -> 0 limit, the
 suffix closed form of the reverse direction, torch's conv1d for the conv
-prologue and the flip identity of the reverse direction.  The pages print no worked numeric
+prologue and the flip identity of the reverse direction; ``bwd`` by torch
+autograd over a plain fp64 loop of the recurrence and by central finite
+differences of ``fwd`` on dyadic inputs.  The pages print no worked numeric
 example, so no value is pinned to a number printed on the pages.
 """
 from __future__ import annotations
@@ -55,6 +57,9 @@ def _load():
         lib.oracle_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
                                       I64, I64, I64, I64, ctypes.c_int, P, P, I64, ctypes.c_int]
         lib.oracle_fwd_ex.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
+                                   P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int]
+        lib.oracle_bwd.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P,
                                             I64, I64, I64, ctypes.c_int]
         lib.oracle_state_update.restype = ctypes.c_int
@@ -112,6 +117,37 @@ def fwd(u, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None, delta_softplu
     if rc != 0:
         raise RuntimeError("oracle_fwd failed with code %d" % rc)
     return y, h_last
+
+
+def bwd(u, delta, A, Bm, Cm, dy, D_skip=None, z=None, delta_bias=None, delta_softplus=True,
+        h0=None, dh_last=None, threads: Optional[int] = None):
+    """fp64 gradients of ``fwd`` (Euler, forward direction, no prologue) for the
+    upstream gradients dy (batch, L, dim) and dh_last (batch, dim, N) or None.
+
+    Returns a dict of float64 arrays: du, ddelta, dz (None without z), dA, dB,
+    dC, dD, dbias, dh0."""
+    u, delta, A, Bm, Cm, dy = map(_f32, (u, delta, A, Bm, Cm, dy))
+    D_skip, z, delta_bias = map(_f32, (D_skip, z, delta_bias))
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and dy.shape == u.shape and A.shape == (dim, N)
+    assert Bm.shape == (batch, L, N) and Cm.shape == (batch, L, N)
+    assert z is None or z.shape == u.shape
+    h0a = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    dhl = None if dh_last is None else np.ascontiguousarray(dh_last, dtype=np.float64)
+    out = dict(du=np.empty((batch, L, dim)), ddelta=np.empty((batch, L, dim)),
+               dz=np.empty((batch, L, dim)) if z is not None else None,
+               dA=np.empty((dim, N)), dB=np.empty((batch, L, N)), dC=np.empty((batch, L, N)),
+               dD=np.empty(dim), dbias=np.empty(dim), dh0=np.empty((batch, dim, N)))
+    rc = _load().oracle_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip),
+                            _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0a),
+                            _ptr(dy), _ptr(dhl), _ptr(out["du"]), _ptr(out["ddelta"]),
+                            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                            _ptr(out["dz"]), _ptr(out["dbias"]), _ptr(out["dh0"]),
+                            batch, L, dim, N, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_bwd failed with code %d" % rc)
+    return out
 
 
 def state_update(state, u, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None,

@@ -75,7 +75,7 @@ static double step_delta(double raw, const float *delta_bias, int64_t d, int del
     return delta_softplus ? softplus(x) : x;
 }
 
-int oracle_abi_version(void) { return 2; }
+int oracle_abi_version(void) { return 3; }
 
 enum { ORACLE_ZOH_EXACT = 1, ORACLE_REVERSE = 2 };
 
@@ -213,4 +213,158 @@ int oracle_state_update(double *state, const float *u, const float *delta, const
         y[p] = yv;
     }
     return 0;
+}
+
+/*
+ * Gradients of oracle_fwd (Euler B_bar, forward direction, no prologue) for
+ * an upstream gradient dy of y and, optionally, dh_last of h_last.
+ *
+ * This is reverse-mode differentiation of the recurrence written out step by
+ * step (the backward pass that the Gu & Dao deep-reading report, §2.4, and
+ * the selection-mechanism article, §3.4, pair with the fused forward: the
+ * states are recomputed, here simply by a stored forward loop).  With
+ * ypre_t = sum_n C_t[n] h_t[n] + D u_t and y_t = ypre_t * SiLU(z_t):
+ *   dypre_t  = dy_t * SiLU(z_t)
+ *   dz_t     = dy_t * ypre_t * SiLU'(z_t)
+ *   lambda_t = dh_t (total adjoint of h_t)
+ *            = C_t dypre_t + A_bar_{t+1} lambda_{t+1}   (lambda_L-1 gets + dh_last)
+ *   dB_t[n] += lambda_t[n] Delta_t u_t                    (summed over channels)
+ *   dC_t[n] += dypre_t h_t[n]                             (summed over channels)
+ *   du_t     = dypre_t D + Delta_t sum_n lambda_t[n] B_t[n]
+ *   dDelta_t = sum_n lambda_t[n] (A[n] A_bar_t[n] h_{t-1}[n] + B_t[n] u_t)
+ *   dA[n]   += lambda_t[n] Delta_t A_bar_t[n] h_{t-1}[n]  (summed over batch, t)
+ *   dD      += dypre_t u_t
+ *   ddelta_t = dDelta_t * sigmoid(Delta_raw + bias)  (softplus; else dDelta_t)
+ *   dbias   += ddelta_t
+ *   dh0      = A_bar_0 lambda_0
+ *
+ * Inputs as oracle_fwd, plus dy (batch, L, dim) fp32 and dh_last
+ * (batch, dim, N) double or NULL.  Outputs (all double, all written):
+ * du, ddelta, dz (batch, L, dim) (dz only when z is given), dA (dim, N),
+ * dB, dC (batch, L, N), dD, dbias (dim), dh0 (batch, dim, N).
+ * Threads split the channels; dB and dC are summed from per-thread buffers.
+ */
+int oracle_bwd(const float *u, const float *delta, const float *A,
+               const float *Bm, const float *Cm, const float *D_skip,
+               const float *z, const float *delta_bias, int delta_softplus,
+               const double *h0, const float *dy, const double *dh_last,
+               double *du, double *ddelta, double *dA, double *dB, double *dC,
+               double *dD, double *dz, double *dbias, double *dh0,
+               int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads)
+{
+    if (batch < 1 || L < 1 || dim < 1 || N < 1)
+        return 1;
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    const int64_t bln = batch * L * N;
+    int nth = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        nth = omp_get_num_threads();
+    }
+    double *accB = (double *)calloc((size_t)nth * bln, sizeof(double));
+    double *accC = (double *)calloc((size_t)nth * bln, sizeof(double));
+    if (!accB || !accC) {
+        free(accB);
+        free(accC);
+        return 2;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        const int tid = omp_get_thread_num();
+        double *myB = accB + (size_t)tid * bln;
+        double *myC = accC + (size_t)tid * bln;
+        double *hs = (double *)malloc((size_t)(L + 1) * N * sizeof(double));
+        double *lam = (double *)malloc((size_t)N * sizeof(double));
+        if (!hs || !lam) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t d = 0; d < dim; ++d) {
+                double sD = 0.0, sbias = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    dA[d * N + n] = 0.0;
+                const double Dd = D_skip ? (double)D_skip[d] : 0.0;
+                for (int64_t b = 0; b < batch; ++b) {
+                    /* forward, keeping every state: hs[t+1] = h_t, hs[0] = h0 */
+                    for (int64_t n = 0; n < N; ++n)
+                        hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+                    for (int64_t t = 0; t < L; ++t) {
+                        int64_t e = (b * L + t) * dim + d;
+                        const float *Bt = Bm + (b * L + t) * N;
+                        double dt = step_delta((double)delta[e], delta_bias, d, delta_softplus);
+                        double ut = (double)u[e];
+                        for (int64_t n = 0; n < N; ++n)
+                            hs[(t + 1) * N + n] = exp(dt * (double)A[d * N + n]) * hs[t * N + n] +
+                                                  dt * (double)Bt[n] * ut;
+                    }
+                    /* backward */
+                    for (int64_t n = 0; n < N; ++n)
+                        lam[n] = dh_last ? dh_last[(b * dim + d) * N + n] : 0.0;
+                    for (int64_t t = L - 1; t >= 0; --t) {
+                        int64_t e = (b * L + t) * dim + d;
+                        const float *Bt = Bm + (b * L + t) * N;
+                        const float *Ct = Cm + (b * L + t) * N;
+                        double x = (double)delta[e] + (delta_bias ? (double)delta_bias[d] : 0.0);
+                        double dt = delta_softplus ? softplus(x) : x;
+                        double ut = (double)u[e];
+                        const double *ht = hs + (t + 1) * N, *hp = hs + t * N;
+                        double ypre = Dd * ut;
+                        for (int64_t n = 0; n < N; ++n)
+                            ypre += (double)Ct[n] * ht[n];
+                        double dyt = (double)dy[e], dypre = dyt;
+                        if (z) {
+                            double zt = (double)z[e];
+                            double sg = 1.0 / (1.0 + exp(-zt));
+                            dypre = dyt * zt * sg;
+                            dz[e] = dyt * ypre * sg * (1.0 + zt * (1.0 - sg));
+                        }
+                        double sLB = 0.0, dDelta = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            double an = (double)A[d * N + n];
+                            double abar = exp(dt * an);
+                            /* lam holds the adjoint arriving from t+1 (already
+                               multiplied by A_bar_{t+1}); add this step's readout */
+                            double l = lam[n] + (double)Ct[n] * dypre;
+                            myC[(b * L + t) * N + n] += dypre * ht[n];
+                            myB[(b * L + t) * N + n] += l * dt * ut;
+                            sLB += l * (double)Bt[n];
+                            dDelta += l * an * abar * hp[n];
+                            dA[d * N + n] += l * dt * abar * hp[n];
+                            lam[n] = abar * l;
+                        }
+                        dDelta += sLB * ut;
+                        du[e] = dypre * Dd + dt * sLB;
+                        double ddl = delta_softplus ? dDelta / (1.0 + exp(-x)) : dDelta;
+                        ddelta[e] = ddl;
+                        sbias += ddl;
+                        sD += dypre * ut;
+                    }
+                    for (int64_t n = 0; n < N; ++n)
+                        dh0[(b * dim + d) * N + n] = lam[n];
+                }
+                dD[d] = sD;
+                dbias[d] = sbias;
+            }
+        }
+        free(hs);
+        free(lam);
+    }
+    if (!bad) {
+        for (int64_t i = 0; i < bln; ++i) {
+            double sb = 0.0, sc = 0.0;
+            for (int k = 0; k < nth; ++k) {
+                sb += accB[(size_t)k * bln + i];
+                sc += accC[(size_t)k * bln + i];
+            }
+            dB[i] = sb;
+            dC[i] = sc;
+        }
+    }
+    free(accB);
+    free(accC);
+    return bad ? 2 : 0;
 }
