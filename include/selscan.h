@@ -25,6 +25,13 @@
  *                        conv1d + SiLU that precedes the scan in the Mamba block
  *                        (tutorial §3.3 and its §4.2 listing), fused as a prologue.
  *
+ *  selscan_bwd           gradients of selscan_fwd with respect to every input
+ *                        (u, Delta_raw, A, B, C, D, z, the Delta bias and h0) for
+ *                        an upstream gradient of y (and of h_last).  The states
+ *                        are recomputed, not stored by the forward: Gu & Dao
+ *                        deep-reading report §2.4 (recomputation in the backward
+ *                        pass), selection-mechanism article (discosf.com) §3.4.
+ *
  *  selscan_state_update  one decode step of the same recurrence on a resident
  *                        state: constant memory and O(1) work per token, one
  *                        state per sample.  Sources: Mamba tutorial §5.1 table
@@ -77,7 +84,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 2
+#define SELSCAN_ABI_VERSION 3
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -187,6 +194,57 @@ int selscan_fwd_ex(const void *u, const void *delta, const float *A,
                    int flags, const float *conv_weight, const float *conv_bias,
                    int64_t conv_width,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace selscan_bwd needs for this shape (never 0 for a
+ * valid shape; 0 for invalid arguments).  It holds the part summaries of the
+ * forward and of the adjoint, the recomputation checkpoints (the state at the
+ * start of every 4-step chunk: batch * ceil(dim/64) * ceil(L/4) * N * 256
+ * bytes) and the partial sums of the reduced gradients.  No initialisation.
+ */
+size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype);
+
+/*
+ * Backward of selscan_fwd (B_bar = Delta B, forward direction).  With
+ * ypre_t = C_t.h_t + D u_t, y_t = ypre_t SiLU(z_t), dypre_t = dy_t SiLU(z_t)
+ * and the adjoint lambda_t = C_t dypre_t + exp(Delta_{t+1} A) lambda_{t+1}
+ * (plus dh_last at t = L-1), it returns the gradient of
+ *     sum(dy * y) + sum(dh_last * h_last)
+ * with respect to each input:
+ *   du[b,t,d]      = dypre D[d] + Delta sum_n lambda[n] B_t[n]
+ *   ddelta[b,t,d]  = dDelta * sigmoid(Delta_raw + bias)  (dDelta with softplus off),
+ *                    dDelta = sum_n lambda[n] (A[d,n] A_bar[n] h_{t-1}[n] + B_t[n] u)
+ *   dA[d,n]        = sum_{b,t} lambda[n] Delta A_bar[n] h_{t-1}[n]
+ *   dB[b,t,n]      = sum_d lambda[n] Delta u        dC[b,t,n] = sum_d dypre h_t[n]
+ *   dD[d]          = sum_{b,t} dypre u              ddelta_bias[d] = sum_{b,t} ddelta
+ *   dz[b,t,d]      = dy ypre SiLU'(z)               dh0[b,d,n] = A_bar_0[n] lambda_0[n]
+ *
+ *   inputs        as selscan_fwd (u, delta, A, Bm, Cm, D_skip, z, delta_bias,
+ *                 delta_softplus, h0), and
+ *   dy            (batch, L, dim)  dtype   upstream gradient of y
+ *   dh_last       (batch, dim, N)  fp32    upstream gradient of h_last; NULL = 0
+ *   du, ddelta    (batch, L, dim)  dtype   written
+ *   dz            (batch, L, dim)  dtype   written; required when z is given,
+ *                                          ignored when z is NULL
+ *   dA            (dim, N)         fp32    written
+ *   dB, dC        (batch, L, N)    fp32    written
+ *   dD, ddelta_bias (dim)          fp32    written; NULL to skip (defined even
+ *                                          when D_skip / delta_bias are NULL)
+ *   dh0           (batch, dim, N)  fp32    written; NULL to skip
+ *   workspace     >= selscan_bwd_workspace_bytes(...), 16-byte aligned
+ *
+ * dB, dC, dA, dD and ddelta_bias are sums in a fixed order (bitwise
+ * repeatable).  Errors as selscan_fwd; every output must be disjoint from
+ * every input and from the other outputs (SELSCAN_ERR_ALIAS).
+ */
+int selscan_bwd(const void *u, const void *delta, const float *A,
+                const void *Bm, const void *Cm, const float *D_skip,
+                const void *z, const float *delta_bias, int delta_softplus,
+                const float *h0, const void *dy, const float *dh_last,
+                void *du, void *ddelta, float *dA, float *dB, float *dC,
+                float *dD, void *dz, float *ddelta_bias, float *dh0,
+                int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step, updating `state` in place:

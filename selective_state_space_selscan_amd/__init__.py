@@ -9,6 +9,8 @@ is no CPU fallback.  If ``libselscan.so`` is missing, every call raises.
     y, h_last = selscan_fwd(..., return_last_state=True)
     y = selscan_fwd_ex(..., flags=SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_ZOH_EXACT,
                        conv_weight=w, conv_bias=b)
+    grads = selscan_bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, h0=h0,
+                        dh_last=dh_last)
     y = selscan_state_update(state, u, delta, A, Bm, Cm, D_skip, z, delta_bias)
 """
 from ._abi import (  # noqa: F401
@@ -20,6 +22,8 @@ from ._abi import (  # noqa: F401
     SelscanError,
     lib,
     lib_path,
+    selscan_bwd,
+    selscan_bwd_workspace_bytes,
     selscan_fwd,
     selscan_fwd_ex,
     selscan_fwd_workspace_bytes,

@@ -62,6 +62,12 @@ def lib():
         L.selscan_fwd_ex.restype = I
         L.selscan_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I,
                                      I, P, P, I64, P, ctypes.c_size_t, P]
+        L.selscan_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.selscan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+        L.selscan_bwd.restype = I
+        L.selscan_bwd.argtypes = [P] * 12 + [P] * 9 + [I64, I64, I64, I64, I, P,
+                                                      ctypes.c_size_t, P]
+        L.selscan_bwd.argtypes[8] = I
         L.selscan_state_update.restype = I
         L.selscan_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
         _lib = L
@@ -198,6 +204,62 @@ def _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, return_
     if rc != 0:
         raise SelscanError(rc, name, L_.selscan_last_hip_error())
     return (y, h_last) if return_last_state else y
+
+
+def selscan_bwd_workspace_bytes(batch: int, L: int, dim: int, N: int, dtype: int) -> int:
+    return int(lib().selscan_bwd_workspace_bytes(batch, L, dim, N, dtype))
+
+
+def selscan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                Cm: torch.Tensor, dy: torch.Tensor, D_skip: Optional[torch.Tensor] = None,
+                z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                dh_last: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> dict:
+    """Gradients of ``selscan_fwd`` through ``selscan_bwd`` (asynchronous on the
+    stream).  dy: (batch, L, dim) in the input dtype; dh_last: (batch, dim, N)
+    float32 or None.  Returns a dict with du, ddelta, dz (None without z) in the
+    input dtype and dA, dB, dC, dD, ddelta_bias, dh0 in float32."""
+    L_ = lib()
+    dev = u.device
+    dt = u.dtype
+    code = _dtype_code(u)
+    batch, L, dim = u.shape
+    N = A.shape[-1]
+    u = _prep(u, dt, dev, "u", (batch, L, dim))
+    delta = _prep(delta, dt, dev, "delta", (batch, L, dim))
+    Bm = _prep(Bm, dt, dev, "Bm", (batch, L, N))
+    Cm = _prep(Cm, dt, dev, "Cm", (batch, L, N))
+    z = _prep(z, dt, dev, "z", (batch, L, dim))
+    dy = _prep(dy, dt, dev, "dy", (batch, L, dim))
+    A = _prep(A, torch.float32, dev, "A", (dim, N))
+    D_skip = _prep(D_skip, torch.float32, dev, "D_skip", (dim,))
+    delta_bias = _prep(delta_bias, torch.float32, dev, "delta_bias", (dim,))
+    h0 = _prep(h0, torch.float32, dev, "h0", (batch, dim, N))
+    dh_last = _prep(dh_last, torch.float32, dev, "dh_last", (batch, dim, N))
+    f32 = torch.float32
+    g = dict(du=torch.empty((batch, L, dim), dtype=dt, device=dev),
+             ddelta=torch.empty((batch, L, dim), dtype=dt, device=dev),
+             dz=torch.empty((batch, L, dim), dtype=dt, device=dev) if z is not None else None,
+             dA=torch.empty((dim, N), dtype=f32, device=dev),
+             dB=torch.empty((batch, L, N), dtype=f32, device=dev),
+             dC=torch.empty((batch, L, N), dtype=f32, device=dev),
+             dD=torch.empty((dim,), dtype=f32, device=dev),
+             ddelta_bias=torch.empty((dim,), dtype=f32, device=dev),
+             dh0=torch.empty((batch, dim, N), dtype=f32, device=dev))
+    ws_bytes = int(L_.selscan_bwd_workspace_bytes(batch, L, dim, N, code))
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    rc = L_.selscan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
+                        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy),
+                        _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                        _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, L, dim, N, code,
+                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(dev, stream))
+    if rc != 0:
+        raise SelscanError(rc, "selscan_bwd", L_.selscan_last_hip_error())
+    return g
 
 
 def selscan_state_update(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor,

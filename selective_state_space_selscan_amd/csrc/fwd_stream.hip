@@ -73,6 +73,48 @@ hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream)
                         : launch_default<float>(a, p, summ, stream);
 }
 
+namespace {
+
+template <int N, typename TIO>
+hipError_t summaries_n(const FwdArgs &a, const StreamPlan &p, float *summ, hipStream_t s)
+{
+    using namespace stream;
+    const ExtParams none = {nullptr, nullptr, 0, 0};
+    const int64_t waves = p.groups * (p.parts - 1);
+    if (waves <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((fwd_stream_kernel<N, true, 0, TIO>),
+                       dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kLanes * kWavesPerBlock), 0, s, (const TIO *)a.u,
+                       (const TIO *)a.delta, (const TIO *)nullptr, (TIO *)nullptr, a.A,
+                       (const TIO *)a.Bm, (const TIO *)a.Cm, (const float *)nullptr,
+                       a.delta_bias, a.delta_softplus, (const float *)nullptr, (float *)nullptr,
+                       summ, a.L, a.dim, p.groups, p.parts, p.part_len, none);
+    return hipGetLastError();
+}
+
+template <typename TIO>
+hipError_t summaries_t(const FwdArgs &a, const StreamPlan &p, float *summ, hipStream_t s)
+{
+    switch (a.N) {
+    case 4: return summaries_n<4, TIO>(a, p, summ, s);
+    case 8: return summaries_n<8, TIO>(a, p, summ, s);
+    case 16: return summaries_n<16, TIO>(a, p, summ, s);
+    case 32: return summaries_n<32, TIO>(a, p, summ, s);
+    case 64: return summaries_n<64, TIO>(a, p, summ, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace
+
+hipError_t launch_fwd_summaries(const FwdArgs &a, const StreamPlan &p, float *summ,
+                                hipStream_t stream)
+{
+    return a.dtype == 1 ? summaries_t<uint16_t>(a, p, summ, stream)
+                        : summaries_t<float>(a, p, summ, stream);
+}
+
 hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream)
 {
     const bool zoh = (e.flags & kFwdFlagZohExact) != 0;

@@ -83,6 +83,27 @@ SELSCAN_DECLARE_EXT(32)
 SELSCAN_DECLARE_EXT(64)
 #undef SELSCAN_DECLARE_EXT
 
+// Forward part summaries alone (the summary pass of the streaming forward,
+// default instantiation) into summ: (groups, parts - 1, N + 1, 64) fp32.
+hipError_t launch_fwd_summaries(const FwdArgs &a, const StreamPlan &p, float *summ,
+                                hipStream_t stream);
+
+// Backward (gradients of the default forward).  `fwd` carries the forward's
+// inputs, dtype, sizes and the workspace; y, h_last, h0-independent fields of
+// it are unused.
+struct BwdArgs {
+    FwdArgs fwd;
+    const void *dy;         // (batch, L, dim) dtype
+    const float *dh_last;   // (batch, dim, N) or null
+    void *du, *ddelta, *dz; // (batch, L, dim) dtype; dz only with z
+    float *dA;              // (dim, N)
+    float *dB, *dC;         // (batch, L, N)
+    float *dD, *ddelta_bias;// (dim) or null
+    float *dh0;             // (batch, dim, N) or null
+};
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+
 // Decode step.
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);
 

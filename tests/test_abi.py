@@ -43,8 +43,8 @@ def header_constant(name):
 def test_library_exports_every_declared_symbol():
     L = ss.lib()
     names = header_functions()
-    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_state_update",
-            "selscan_fwd_workspace_bytes"} <= set(names)
+    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_bwd", "selscan_state_update",
+            "selscan_fwd_workspace_bytes", "selscan_bwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), "missing export " + n
     assert L.selscan_abi_version() == header_constant("SELSCAN_ABI_VERSION")
@@ -175,6 +175,64 @@ def test_fwd_ex_workspace_checked_when_needed():
         args = fwd_ex_args(flags=3, conv_width=4, conv_w=fake(13), batch=1, L=131072, dim=2048,
                            workspace=ws, workspace_bytes=nbytes)
         assert L.selscan_fwd_ex(*args) == ERR_WS
+
+
+def bwd_args(**kw):
+    a = dict(u=fake(1), delta=fake(2), A=fake(3), Bm=fake(4), Cm=fake(5), D_skip=fake(6),
+             z=fake(7), delta_bias=fake(8), delta_softplus=1, h0=fake(9), dy=fake(10),
+             dh_last=fake(11), du=fake(12), ddelta=fake(13), dA=fake(14), dB=fake(15),
+             dC=fake(16), dD=fake(17), dz=fake(18), ddelta_bias=fake(19), dh0=fake(20),
+             batch=2, L=64, dim=128, N=16, dtype=1, workspace=fake(21),
+             workspace_bytes=1 << 34, stream=None)
+    a.update(kw)
+    order = ["u", "delta", "A", "Bm", "Cm", "D_skip", "z", "delta_bias", "delta_softplus", "h0",
+             "dy", "dh_last", "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh0",
+             "batch", "L", "dim", "N", "dtype", "workspace", "workspace_bytes", "stream"]
+    return [a[k] for k in order]
+
+
+INVALID_BWD = [
+    ("dtype", dict(dtype=5), ERR_DTYPE),
+    ("L0", dict(L=0), ERR_SHAPE),
+    ("N0", dict(N=0), ERR_SHAPE),
+    ("overflow", dict(batch=1 << 40, L=1 << 20, dim=1 << 10), ERR_SHAPE),
+    ("dy_null", dict(dy=None), ERR_NULL),
+    ("du_null", dict(du=None), ERR_NULL),
+    ("ddelta_null", dict(ddelta=None), ERR_NULL),
+    ("dA_null", dict(dA=None), ERR_NULL),
+    ("dB_null", dict(dB=None), ERR_NULL),
+    ("dC_null", dict(dC=None), ERR_NULL),
+    ("dz_null_with_z", dict(dz=None), ERR_NULL),
+    ("N12", dict(N=12), ERR_UNSUP),
+    ("dim_too_large", dict(dim=(1 << 24) + 64, batch=1, L=2), ERR_UNSUP),
+    ("misaligned_dy", dict(dy=ctypes.c_void_p(BASE + 10 * STEP + 4)), ERR_UNSUP),
+    ("misaligned_dh0", dict(dh0=ctypes.c_void_p(BASE + 20 * STEP + 8)), ERR_UNSUP),
+    ("no_workspace", dict(workspace=None), ERR_WS),
+    ("small_workspace", dict(workspace_bytes=1024), ERR_WS),
+    ("du_aliases_u", dict(du=ctypes.c_void_p(BASE + STEP + 128)), ERR_ALIAS),
+    ("dB_aliases_Bm", dict(dB=ctypes.c_void_p(BASE + 4 * STEP + 64)), ERR_ALIAS),
+    ("dA_aliases_dD", dict(dD=ctypes.c_void_p(BASE + 14 * STEP + 256)), ERR_ALIAS),
+    ("dh0_aliases_workspace", dict(dh0=ctypes.c_void_p(BASE + 21 * STEP + 4096)), ERR_ALIAS),
+    ("ddelta_aliases_dz", dict(dz=ctypes.c_void_p(BASE + 13 * STEP + 512)), ERR_ALIAS),
+]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("name,kw,status", INVALID_BWD, ids=[c[0] for c in INVALID_BWD])
+def test_bwd_rejects_invalid_arguments(name, kw, status):
+    L = ss.lib()
+    assert L.selscan_bwd(*bwd_args(**kw)) == status
+    assert L.selscan_last_hip_error() == 0
+
+
+def test_bwd_workspace_size():
+    L = ss.lib()
+    # checkpoints alone: batch * ceil(dim/64) * ceil(L/4) * N * 256 bytes
+    need = L.selscan_bwd_workspace_bytes(2, 64, 128, 16, 1)
+    assert need >= 2 * 2 * 16 * 16 * 256
+    assert L.selscan_bwd_workspace_bytes(2, 64, 128, 16, 7) == 0
+    assert L.selscan_bwd_workspace_bytes(2, 64, 128, 12, 1) == 0
+    assert L.selscan_bwd_workspace_bytes(0, 64, 128, 16, 1) == 0
 
 
 def step_args(**kw):
