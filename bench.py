@@ -3,6 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --pmc-run            # workload for rocprofv3 --pmc (see below)
     python bench.py --parse-pmc FETCH_DIR WRITE_DIR   # -> profiles/traffic_<workload>.json
+    python bench.py --pass bwd           # the backward (selscan_bwd) on the same workload
+    python bench.py --variant zoh,rev,conv4   # forward variants through selscan_fwd_ex
 
 One step = one selscan_fwd call over one batch of the workload.  The default
 workload is one Mamba-130M layer: batch 8, L 2048, D 1536, N 16, bf16 inputs,
@@ -79,11 +81,15 @@ def algorithmic_valu_slots(N, gate, es):
     return per
 
 
+# The sources of the forward kernels the counters are taken on.
+FWD_KERNEL_SOURCES = ("fwd_stream.hip", "fwd_stream_impl.hpp", "buffer_io.hpp", "device_math.hpp")
+
+
 def source_digest():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_selscan_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    for name in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "selective_state_space_selscan_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -270,6 +276,95 @@ def bench_decode(w, steps, warmup):
     print(json.dumps(res), flush=True)
 
 
+def bwd_valu_slots(N, gate, es):
+    """fp32 VALU slots per (b, l, d) element of the backward as built: the
+    chunk's states recomputed from a checkpoint (3 N: A_bar, Delta u B, FMA),
+    the adjoint step (11 N: lambda, readout, A_bar h_{t-1}, its product with
+    lambda, the dDelta and dA sums, lambda.B, the dB and dC terms, A_bar,
+    the carry) and about 60 per element (softplus and sigmoid twice, SiLU and
+    its derivative, widening, the per-element gradients).  The checkpoint
+    and summary passes and the LDS reductions are extra work of the
+    recomputation scheme, not counted."""
+    return 14 * N + 60
+
+
+def bench_bwd(w, args):
+    """``steps`` selscan_bwd calls on the workload (upstream gradient dy
+    seeded, no dh_last), inputs resident in HBM, one workspace."""
+    import torch
+
+    import selscan_inputs as si
+    import selective_state_space_selscan_amd as ss
+    dev = torch.device("cuda:0")
+    inp, sets = make_inputs(w, dev, 1)
+    t = sets[0]
+    rng = np.random.default_rng([w.seed, 4242])
+    dy = torch.from_numpy(rng.standard_normal((w.batch, w.L, w.dim), dtype=np.float32)).to(dev)
+    dy = dy.to(t["u"].dtype)
+    code = ss.SELSCAN_BF16 if w.dtype == si.BF16 else ss.SELSCAN_F32
+    ws = torch.empty(ss.selscan_bwd_workspace_bytes(w.batch, w.L, w.dim, w.N, code),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"], t["z"],
+                       t["delta_bias"], True, None, None, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    es = 2 if w.dtype == si.BF16 else 4
+    elems = w.batch * w.L * w.dim
+    call_mean = float(np.mean(call_ms))
+    slots = bwd_valu_slots(w.N, w.gate, es) * elems
+    # bytes the backward must move: the forward's inputs once, dy, and the
+    # gradients du, ddelta, dz (dtype) and dB, dC (fp32) once
+    nb = (elems * ((3 if w.gate else 2) * es + es + (3 if w.gate else 2) * es)
+          + 2 * w.batch * w.L * w.N * (es + 4) + w.dim * w.N * 8 + 4 * w.dim * 4)
+    achieved = slots / (call_mean * 1e-3) / 1e9
+    res = {
+        "metric": "selective-scan bwd elements(B*L*D)/s, 1 GPU",
+        "value": elems / (wall / args.steps), "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * wall / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == si.BF16 else "f32", "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "pass": "bwd", "batch": w.batch, "L": w.L, "dim": w.dim,
+                   "N": w.N, "gate": w.gate},
+        "call_ms": {"mean": call_mean, "p50": float(np.median(call_ms))},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_SLOTS / 1e9,
+                     "unit": "G VALU lane-slots/s", "frac": achieved * 1e9 / VALU_PEAK_SLOTS,
+                     "traffic": None, "kernel": "selscan_bwd call (all passes)",
+                     "algorithmic_slots_per_element": bwd_valu_slots(w.N, w.gate, es),
+                     "algorithmic_bytes_per_call": nb,
+                     "hbm_gbps_of_call": nb / (call_mean * 1e-3) / 1e9},
+    }
+    print(json.dumps(res), flush=True)
+
+
+VARIANT_FLAGS = {"zoh": 1, "rev": 2}
+
+
+def parse_variant(spec):
+    """'zoh,rev,conv4' -> (flags, conv width)."""
+    flags, k = 0, 0
+    for part in filter(None, (spec or "").split(",")):
+        if part.startswith("conv"):
+            k = int(part[4:] or 4)
+        else:
+            flags |= VARIANT_FLAGS[part]
+    return flags, k
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +375,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--variant", default="", help="forward variants: zoh, rev, convK")
     args = ap.parse_args()
 
     import selscan_inputs as si
@@ -297,6 +394,10 @@ def main():
     if args.pmc_run:
         pmc_run(w)
         return
+    if args.which == "bwd":
+        bench_bwd(w, args)
+        return
+    vflags, vconv = parse_variant(args.variant)
 
     import torch
 
@@ -314,9 +415,20 @@ def main():
     wss = [torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
            for _ in range(args.rotate)]
     stream = torch.cuda.current_stream(dev)
+    conv_w = conv_b = None
+    if vconv:
+        cw, cb = si.conv_params(w.dim, vconv, w.seed)
+        conv_w, conv_b = torch.from_numpy(cw).to(dev), torch.from_numpy(cb).to(dev)
 
     def step(i):
         t = sets[i % args.rotate]
+        if args.variant:
+            ss.selscan_fwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                              t["delta_bias"], True, None, return_last_state=w.want_last_state,
+                              flags=vflags, conv_weight=conv_w, conv_bias=conv_b,
+                              y=ys[i % args.rotate], h_last=hls[i % args.rotate],
+                              workspace=wss[i % args.rotate], stream=stream)
+            return
         ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
                        t["delta_bias"], True, None, return_last_state=w.want_last_state,
                        y=ys[i % args.rotate], h_last=hls[i % args.rotate],
@@ -360,6 +472,7 @@ def main():
                 "dt log-uniform [1e-3,0.1], A=-(n+1), D=1)",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "dim": w.dim, "N": w.N,
                    "gate": w.gate, "state": "fp32", "rotating_input_sets": args.rotate},
+        **({"variant": args.variant} if args.variant else {}),
         "hbm_gbps": abytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": abytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "call_ms": {"mean": call_mean, "p10": float(np.percentile(call_ms, 10)),
@@ -372,7 +485,11 @@ def main():
                      "algorithmic_bytes_per_call": abytes,
                      "hbm_gbps_of_call": abytes / (call_mean * 1e-3) / 1e9},
     }
-    if not args.no_cpu:
+    if args.variant:
+        result["roofline"]["traffic"] = None
+        result["roofline"]["kernel"] = "selscan_fwd_ex call (%s); slots of the default path" \
+            % args.variant
+    if not args.no_cpu and not args.variant:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)
 

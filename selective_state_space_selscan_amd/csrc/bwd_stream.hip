@@ -388,6 +388,9 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
         const float sz = sigmoid(zt);
         const float gz = gated ? zt * sz : 1.0f;
         const float dypre = dyt * gz;
+        // factors of the dB, dC terms, zero on lanes past dim (they add nothing)
+        const float du_a = active ? du : 0.0f;
+        const float dypre_a = active ? dypre : 0.0f;
         const float r = POW ? hw_exp2(dt * c.A2_0) : 0.0f;
         float pw = 1.0f;
         float ypre = c.Dd * ut, sLB = 0.0f, wA = 0.0f;
@@ -403,9 +406,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
             dA[n] = fmaf(dt, wq, dA[n]);
             sLB = fmaf(lam, Bn, sLB);
             // this lane's terms of dB_t[n] and dC_t[n]; row n of the LDS tiles
-            // (lanes past dim add nothing)
-            ldsB[n * kLdsStride + lane] = active ? lam * du : 0.0f;
-            ldsC[n * kLdsStride + lane] = active ? dypre * hn : 0.0f;
+            ldsB[n * kLdsStride + lane] = lam * du_a;
+            ldsC[n * kLdsStride + lane] = dypre_a * hn;
             const float a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
             g[n] = a * lam;
         }
@@ -531,48 +533,44 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N <= 32 
 // ---------------------------------------------------------------------------
 // 5. reductions of the partials (fixed order)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float *__restrict__ pB,
-                                                            const float *__restrict__ pC,
-                                                            float *__restrict__ dB,
-                                                            float *__restrict__ dC, int64_t count,
-                                                            int64_t gpr)
+// out[i] = sum_k in[k * P + i] for i < P, k < K: a block of four waves owns 64
+// columns; wave w adds the rows k = w, w + 4, ... (eight loads in flight),
+// then the four sums are added in wave order.
+__global__ __launch_bounds__(256) void bwd_colsum_kernel(const float *__restrict__ in,
+                                                         float *__restrict__ out, int64_t P,
+                                                         int64_t K)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count)
-        return;
-    float sb = 0.0f, sc = 0.0f;
-    for (int64_t k = 0; k < gpr; ++k) {
-        sb += pB[k * count + i];
-        sc += pC[k * count + i];
+    __shared__ float part[4][kLanes];
+    const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * kLanes + lane;
+    float s = 0.0f;
+    if (i < P) {
+        int64_t k = wave;
+        for (; k + 28 < K; k += 32) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = in[(k + 4 * j) * P + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                s += v[j];
+        }
+        for (; k < K; k += 4)
+            s += in[k * P + i];
     }
-    dB[i] = sb;
-    dC[i] = sc;
+    part[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && i < P)
+        out[i] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
 
-__global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
-    const float *__restrict__ pA, const float *__restrict__ pD, const float *__restrict__ pbias,
-    float *__restrict__ dA, float *__restrict__ dD, float *__restrict__ dbias, int64_t dim,
-    int64_t N, int64_t slots)
+hipError_t launch_colsum(const float *in, float *out, int64_t P, int64_t K, hipStream_t s)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t na = dim * N;
-    if (i < na) {
-        float s = 0.0f;
-        for (int64_t k = 0; k < slots; ++k)
-            s += pA[k * na + i];
-        dA[i] = s;
-    } else if (i < na + dim) {
-        const int64_t d = i - na;
-        float sd = 0.0f, sb = 0.0f;
-        for (int64_t k = 0; k < slots; ++k) {
-            sd += pD[k * dim + d];
-            sb += pbias[k * dim + d];
-        }
-        if (dD)
-            dD[d] = sd;
-        if (dbias)
-            dbias[d] = sb;
-    }
+    if (!out || P <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(bwd_colsum_kernel, dim3((unsigned)((P + kLanes - 1) / kLanes)), dim3(256),
+                       0, s, in, out, P, K);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -649,14 +647,13 @@ hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t s)
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int64_t count = a.fwd.batch * a.fwd.L * N;
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                       s, o.pB, o.pC, a.dB, a.dC, count, w.gpr);
-    if ((e = hipGetLastError()) != hipSuccess)
+    const int64_t slots = a.fwd.batch * p.parts;
+    if ((e = launch_colsum(o.pB, a.dB, count, w.gpr, s)) != hipSuccess ||
+        (e = launch_colsum(o.pC, a.dC, count, w.gpr, s)) != hipSuccess ||
+        (e = launch_colsum(o.pA, a.dA, a.fwd.dim * N, slots, s)) != hipSuccess ||
+        (e = launch_colsum(o.pD, a.dD, a.fwd.dim, slots, s)) != hipSuccess ||
+        (e = launch_colsum(o.pbias, a.ddelta_bias, a.fwd.dim, slots, s)) != hipSuccess)
         return e;
-    const int64_t np = a.fwd.dim * N + a.fwd.dim;
-    hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0,
-                       s, o.pA, o.pD, o.pbias, a.dA, a.dD, a.ddelta_bias, a.fwd.dim, (int64_t)N,
-                       a.fwd.batch * p.parts);
     return hipGetLastError();
 }
 
