@@ -100,27 +100,6 @@ __device__ __forceinline__ bool load_A(const float *A, int64_t d, float (&A2)[N]
     return __all(structured);
 }
 
-// x <- exp(A S) x + v, the fold of one part summary (S, v) into a carry.
-template <int N>
-__device__ __forceinline__ void fold_summary(float (&x)[N], const float *s, bool pow_path,
-                                             const float (&A2)[N], float A2_0)
-{
-    const float S = s[0];
-    if (pow_path) {
-        const float e = hw_exp2(A2_0 * S);
-        float pw = 1.0f;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            pw *= e;
-            x[n] = fmaf(pw, x[n], s[(n + 1) * kLanes]);
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n)
-            x[n] = fmaf(hw_exp2(A2[n] * S), x[n], s[(n + 1) * kLanes]);
-    }
-}
-
 __device__ __forceinline__ float sigmoid(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
 
 template <typename TIO>
@@ -302,9 +281,8 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_checkpoint_kernel(
 #pragma unroll
     for (int n = 0; n < N; ++n)
         h[n] = h0 ? h0[(c.b * dim + w.d) * N + n] : 0.0f;
-    for (int q = 0; q < w.part; ++q)
-        fold_summary<N>(h, fsumm + ((w.grp * (parts - 1) + q) * (N + 1)) * kLanes + w.lane,
-                        pow_path, A2, c.A2_0);
+    stream::fold_summaries<N>(h, fsumm + (w.grp * (parts - 1)) * (N + 1) * kLanes + w.lane, 0,
+                              w.part, 1, pow_path, A2, c.A2_0);
     float *ck = ckpt + w.grp * nck * (N * kLanes) + w.lane;
     if (pow_path)
         checkpoint_part<N, true>(u, delta, Bm, c, A2, h, ck);
@@ -498,9 +476,9 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N <= 32 
 #pragma unroll
     for (int n = 0; n < N; ++n)
         g[n] = dh_last ? dh_last[(c.b * dim + w.d) * N + n] : 0.0f;
-    for (int q = parts - 1; q > w.part; --q)
-        fold_summary<N>(g, asumm + ((w.grp * (parts - 1) + (q - 1)) * (N + 1)) * kLanes + w.lane,
-                        pow_path, A2, c.A2_0);
+    // adjoint summary of part q is entry q - 1; fold parts P-1 down to part+1
+    stream::fold_summaries<N>(g, asumm + (w.grp * (parts - 1)) * (N + 1) * kLanes + w.lane,
+                              parts - 2, parts - 1 - w.part, -1, pow_path, A2, c.A2_0);
     float dA[N];
 #pragma unroll
     for (int n = 0; n < N; ++n)

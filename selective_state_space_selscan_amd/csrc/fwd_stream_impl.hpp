@@ -448,6 +448,64 @@ __device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta,
     }
 }
 
+// h <- exp(A S) h + x for one part summary v = (S, x[0..N-1]); for structured
+// A, exp(A[d,n] S) = e^(n+1) with e = exp(A[d,0] S).
+constexpr int kFoldGroup = 4;
+template <int N>
+__device__ __forceinline__ void fold_part_summary(float (&h)[N], const float (&v)[N + 1],
+                                                  bool pow_path, const float (&A2)[N],
+                                                  float A2_0)
+{
+    const float S = v[0];
+    if (pow_path) {
+        const float e = hw_exp2(A2_0 * S);
+        float pw = 1.0f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            pw *= e;
+            h[n] = fmaf(pw, h[n], v[n + 1]);
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            h[n] = fmaf(hw_exp2(A2[n] * S), h[n], v[n + 1]);
+    }
+}
+
+// Folds `count` part summaries into h, the summary indices first, first + dir,
+// ...  sbase points at summary 0 of this lane's channel group (summaries are
+// (N + 1) * 64 floats apart).  The summaries are read kFoldGroup at a time,
+// all loads first, so a wave waits for memory once per group rather than
+// once per part.
+template <int N>
+__device__ __forceinline__ void fold_summaries(float (&h)[N], const float *sbase, int first,
+                                               int count, int dir, bool pow_path,
+                                               const float (&A2)[N], float A2_0)
+{
+    int k0 = 0;
+    for (; k0 + kFoldGroup <= count; k0 += kFoldGroup) {
+        float v[kFoldGroup][N + 1];
+#pragma unroll
+        for (int k = 0; k < kFoldGroup; ++k) {
+            const float *s = sbase + (int64_t)(first + (k0 + k) * dir) * (N + 1) * kLanes;
+#pragma unroll
+            for (int n = 0; n <= N; ++n)
+                v[k][n] = s[n * kLanes];
+        }
+#pragma unroll
+        for (int k = 0; k < kFoldGroup; ++k)
+            fold_part_summary<N>(h, v[k], pow_path, A2, A2_0);
+    }
+    for (; k0 < count; ++k0) {
+        const float *s = sbase + (int64_t)(first + k0 * dir) * (N + 1) * kLanes;
+        float v[N + 1];
+#pragma unroll
+        for (int n = 0; n <= N; ++n)
+            v[n] = s[n * kLanes];
+        fold_part_summary<N>(h, v, pow_path, A2, A2_0);
+    }
+}
+
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for N <= 16;
 // three (at most 168 VGPRs) for the exact-ZOH and conv variants, whose
 // coefficients and taps would spill at 128.
@@ -543,24 +601,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
         h[n] = (!SUMMARY && h0) ? h0[(c.b * dim + d) * N + n] : 0.0f;
     if (!SUMMARY) {
         // h <- exp(A S) h + x for each earlier part (S = its sum of Delta, x =
-        // its end state from zero); for structured A, exp(A[d,n] S) = e^(n+1).
-        for (int q = 0; q < part; ++q) {
-            const float *s = summ + ((grp * (parts - 1) + q) * (N + 1)) * kLanes + lane;
-            const float S = s[0];
-            if (pow_path) {
-                const float e = hw_exp2(c.A2_0 * S);
-                float pw = 1.0f;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    pw *= e;
-                    h[n] = fmaf(pw, h[n], s[(n + 1) * kLanes]);
-                }
-            } else {
-#pragma unroll
-                for (int n = 0; n < N; ++n)
-                    h[n] = fmaf(hw_exp2(A2[n] * S), h[n], s[(n + 1) * kLanes]);
-            }
-        }
+        // its end state from zero), in part order.
+        fold_summaries<N>(h, summ + (grp * (parts - 1)) * (N + 1) * kLanes + lane, 0, part, 1,
+                          pow_path, A2, c.A2_0);
     }
 
     float sdelta = 0.0f;
