@@ -62,6 +62,10 @@ StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim);
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
 
+// Single-pass streaming forward with decoupled look-back (same plan).
+size_t fwd_lookback_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+hipError_t launch_fwd_lookback(const FwdArgs &a, hipStream_t stream);
+
 // Variants of the streaming forward (same plan and workspace).
 constexpr int kFwdFlagZohExact = 1;
 constexpr int kFwdFlagReverse = 2;

@@ -26,10 +26,11 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // forward kernels within 32 bits (at most 16 timesteps x dim x 4 bytes < 2^30).
 const int64_t kMaxDim = (int64_t)1 << 24;
 
-// Forward plans.  Default: the streaming kernel.  SELSCAN_FORCE_PLAN=chunked
-// or =serial selects the workgroup-chunked or the one-lane-per-channel kernel
-// (ablations; all three compute the same recurrence).
-enum Plan { PLAN_STREAM, PLAN_CHUNKED, PLAN_SERIAL };
+// Forward plans.  Default: the two-pass streaming kernel.  SELSCAN_FORCE_PLAN
+// = lookback selects the single-pass streaming kernel with decoupled
+// look-back; = chunked or = serial the workgroup-chunked or the
+// one-lane-per-channel kernel (ablations; all compute the same recurrence).
+enum Plan { PLAN_STREAM, PLAN_LOOKBACK, PLAN_CHUNKED, PLAN_SERIAL };
 
 Plan forced_plan()
 {
@@ -38,6 +39,8 @@ Plan forced_plan()
         return PLAN_SERIAL;
     if (e && strcmp(e, "chunked") == 0)
         return PLAN_CHUNKED;
+    if (e && strcmp(e, "lookback") == 0)
+        return PLAN_LOOKBACK;
     return PLAN_STREAM;
 }
 
@@ -140,6 +143,8 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
         return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
     case PLAN_CHUNKED:
         return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
+    case PLAN_LOOKBACK:
+        return finish_launch(selscan::launch_fwd_lookback(a, (hipStream_t)stream));
     default:
         return finish_launch(selscan::launch_fwd_stream(a, (hipStream_t)stream));
     }
@@ -177,7 +182,9 @@ size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_
         return 0;
     const size_t a = selscan::fwd_chunked_workspace_bytes(batch, L, dim, N);
     const size_t b = selscan::fwd_stream_workspace_bytes(batch, L, dim, N);
-    return a > b ? a : b;
+    const size_t c = selscan::fwd_lookback_workspace_bytes(batch, L, dim, N);
+    const size_t ab = a > b ? a : b;
+    return ab > c ? ab : c;
 }
 
 int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
