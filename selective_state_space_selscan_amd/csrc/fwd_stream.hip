@@ -9,17 +9,18 @@
 namespace selscan {
 
 // SELSCAN_STREAM_PARTS=P overrides the number of sequence parts (tuning knob).
-// Default (measured on MI355X): about 4096 waves (4 per SIMD) when the channel
-// groups are few; with many groups, at least 8 parts (when L allows), since
-// smaller waves balance the tail of the grid better than fewer, longer ones.
-// Parts are whole multiples of kStreamTT steps and at least 4 of them long.
-StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim)
+// Default (measured on MI355X): about one wave per wave slot of the chip (1024
+// SIMDs x the kernel's waves per SIMD) when the channel groups are few; with
+// many groups, at least 8 parts (when L allows), since smaller waves balance
+// the tail of the grid better than fewer, longer ones.  Parts are whole
+// multiples of kStreamTT steps and at least 4 of them long.
+StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd)
 {
     constexpr int kLanes = stream::kLanes;
     constexpr int TT = kStreamTT;
     StreamPlan p;
     p.groups = batch * ((dim + kLanes - 1) / kLanes);
-    const int64_t target_waves = 4096;
+    const int64_t target_waves = 1024 * (int64_t)waves_per_simd;
     int64_t parts = (target_waves + p.groups - 1) / p.groups;
     const int64_t min_parts = L / 256 < 8 ? L / 256 : 8;
     if (parts < min_parts)
@@ -43,7 +44,8 @@ StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim)
 
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N)
 {
-    const StreamPlan p = make_stream_plan(batch, L, dim);
+    // the default plan has the most parts (the variants' plans aim at fewer waves)
+    const StreamPlan p = make_stream_plan(batch, L, dim, 4);
     return p.parts > 1 ? (size_t)p.groups * (p.parts - 1) * (N + 1) * stream::kLanes * 4 + 256 : 0;
 }
 

@@ -507,14 +507,15 @@ __device__ __forceinline__ void fold_summaries(float (&h)[N], const float *sbase
 }
 
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for N <= 16;
-// three (at most 168 VGPRs) for the exact-ZOH and conv variants, whose
-// coefficients and taps would spill at 128.
+// three (at most 168 VGPRs) for the exact-ZOH variants, whose per-state
+// coefficients would spill at 128.  (The conv variant spills a few registers
+// at four waves and is still faster there than at three: measured.)
 template <int N, int VAR>
 constexpr int waves_per_eu()
 {
     if (N > 16)
         return 1;
-    return (VAR & (kVarZoh | kVarConv)) != 0 ? 3 : 4;
+    return (VAR & kVarZoh) != 0 ? 3 : 4;
 }
 
 template <int N, bool SUMMARY, int VAR, typename TIO>
@@ -681,7 +682,9 @@ inline float *summary_buffer(void *workspace)
 template <int N, bool ZOH>
 hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
 {
-    const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim);
+    constexpr int V0 = kVarExt | (ZOH ? kVarZoh : 0);
+    const int occupancy = e.conv_k > 0 ? waves_per_eu<N, V0 | kVarConv>() : waves_per_eu<N, V0>();
+    const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, occupancy);
     float *summ = summary_buffer(a.workspace);
     ExtParams x;
     x.conv_w = e.conv_k > 0 ? e.conv_w : nullptr;

@@ -58,7 +58,8 @@ struct StreamPlan {
     int64_t part_len;   // steps per sequence part
     int parts;
 };
-StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim);
+// waves_per_simd: the kernel's occupancy (the plan aims at one wave per slot).
+StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd = 4);
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
 
