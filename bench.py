@@ -212,8 +212,10 @@ def decode_bytes(batch, dim, N, es, gate):
 def bench_decode(w, steps, warmup):
     """Decode: ``steps`` single-token selscan_state_update calls on the resident
     fp32 state (batch, dim, N).  Warm: back-to-back steps, the 84 MB state may
-    stay in the 256 MB last-level cache.  Cold: a 1 GiB buffer is written before
-    each timed step, so the state comes from HBM."""
+    stay in the 256 MB last-level cache.  Cold: a 1 GiB buffer is read before
+    each timed step, so the state comes from HBM.  (Writing the buffer instead
+    would leave the cache full of dirty lines whose write-back then lands in
+    the timed step.)"""
     import torch
 
     import selscan_inputs as si
@@ -246,8 +248,9 @@ def bench_decode(w, steps, warmup):
     warm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold = []
+    flush.fill_(1.0)
     for i in range(min(steps, 50)):
-        flush.fill_(float(i))
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         step(i)
