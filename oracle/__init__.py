@@ -60,6 +60,10 @@ def _load():
         lib.oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
                                    P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int]
         lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
+                                      P, P, P, P, P, P, P, P, P, I64, I64, I64, I64,
+                                      ctypes.c_int, P, P, I64, P, P, ctypes.c_int]
+        lib.oracle_bwd_ex.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P,
                                             I64, I64, I64, ctypes.c_int]
         lib.oracle_state_update.restype = ctypes.c_int
@@ -120,14 +124,18 @@ def fwd(u, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None, delta_softplu
 
 
 def bwd(u, delta, A, Bm, Cm, dy, D_skip=None, z=None, delta_bias=None, delta_softplus=True,
-        h0=None, dh_last=None, threads: Optional[int] = None):
-    """fp64 gradients of ``fwd`` (Euler, forward direction, no prologue) for the
+        h0=None, dh_last=None, threads: Optional[int] = None, flags: int = 0, conv_w=None,
+        conv_b=None):
+    """fp64 gradients of ``fwd`` (with the same flags and conv prologue) for the
     upstream gradients dy (batch, L, dim) and dh_last (batch, dim, N) or None.
 
-    Returns a dict of float64 arrays: du, ddelta, dz (None without z), dA, dB,
-    dC, dD, dbias, dh0."""
+    Returns a dict of float64 arrays: du (of the raw input when the conv
+    prologue is on), ddelta, dz (None without z), dA, dB, dC, dD, dbias, dh0,
+    and dconv_w, dconv_b (None without the conv prologue)."""
     u, delta, A, Bm, Cm, dy = map(_f32, (u, delta, A, Bm, Cm, dy))
     D_skip, z, delta_bias = map(_f32, (D_skip, z, delta_bias))
+    conv_w, conv_b = _f32(conv_w), _f32(conv_b)
+    conv_k = 0 if conv_w is None else conv_w.shape[1]
     batch, L, dim = u.shape
     N = A.shape[1]
     assert delta.shape == u.shape and dy.shape == u.shape and A.shape == (dim, N)
@@ -138,13 +146,17 @@ def bwd(u, delta, A, Bm, Cm, dy, D_skip=None, z=None, delta_bias=None, delta_sof
     out = dict(du=np.empty((batch, L, dim)), ddelta=np.empty((batch, L, dim)),
                dz=np.empty((batch, L, dim)) if z is not None else None,
                dA=np.empty((dim, N)), dB=np.empty((batch, L, N)), dC=np.empty((batch, L, N)),
-               dD=np.empty(dim), dbias=np.empty(dim), dh0=np.empty((batch, dim, N)))
-    rc = _load().oracle_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip),
-                            _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0a),
-                            _ptr(dy), _ptr(dhl), _ptr(out["du"]), _ptr(out["ddelta"]),
-                            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-                            _ptr(out["dz"]), _ptr(out["dbias"]), _ptr(out["dh0"]),
-                            batch, L, dim, N, threads or default_threads())
+               dD=np.empty(dim), dbias=np.empty(dim), dh0=np.empty((batch, dim, N)),
+               dconv_w=np.empty((dim, conv_k)) if conv_k else None,
+               dconv_b=np.empty(dim) if conv_k else None)
+    rc = _load().oracle_bwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip),
+                               _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0a),
+                               _ptr(dy), _ptr(dhl), _ptr(out["du"]), _ptr(out["ddelta"]),
+                               _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                               _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dbias"]),
+                               _ptr(out["dh0"]), batch, L, dim, N, int(flags), _ptr(conv_w),
+                               _ptr(conv_b), conv_k, _ptr(out["dconv_w"]), _ptr(out["dconv_b"]),
+                               threads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_bwd failed with code %d" % rc)
     return out

@@ -75,7 +75,7 @@ static double step_delta(double raw, const float *delta_bias, int64_t d, int del
     return delta_softplus ? softplus(x) : x;
 }
 
-int oracle_abi_version(void) { return 3; }
+int oracle_abi_version(void) { return 4; }
 
 enum { ORACLE_ZOH_EXACT = 1, ORACLE_REVERSE = 2 };
 
@@ -215,47 +215,77 @@ int oracle_state_update(double *state, const float *u, const float *delta, const
     return 0;
 }
 
+/* d/dDelta of the B_bar coefficient: 1 (Euler) or exp(Delta a) (exact ZOH). */
+static double bbar_coeff_ddt(double dt, double a, int zoh_exact)
+{
+    return zoh_exact ? exp(dt * a) : 1.0;
+}
+
+/* d/da of the exact-ZOH coefficient expm1(Delta a)/a:
+   (Delta a e^(Delta a) - expm1(Delta a)) / a^2, whose limit at a -> 0 is
+   Delta^2 (1/2 + x/3 + x^2/8 + ...) with x = Delta a (series where |x| is small). */
+static double bbar_coeff_da(double dt, double a, int zoh_exact)
+{
+    if (!zoh_exact)
+        return 0.0;
+    double x = dt * a;
+    if (fabs(x) < 1e-3)
+        return dt * dt * (0.5 + x / 3.0 + x * x / 8.0 + x * x * x / 30.0);
+    return (x * exp(x) - expm1(x)) / (a * a);
+}
+
 /*
- * Gradients of oracle_fwd (Euler B_bar, forward direction, no prologue) for
- * an upstream gradient dy of y and, optionally, dh_last of h_last.
+ * Gradients of oracle_fwd_ex for an upstream gradient dy of y and, optionally,
+ * dh_last of h_last.
  *
  * This is reverse-mode differentiation of the recurrence written out step by
  * step (the backward pass that the Gu & Dao deep-reading report, §2.4, and
  * the selection-mechanism article, §3.4, pair with the fused forward: the
- * states are recomputed, here simply by a stored forward loop).  With
- * ypre_t = sum_n C_t[n] h_t[n] + D u_t and y_t = ypre_t * SiLU(z_t):
- *   dypre_t  = dy_t * SiLU(z_t)
- *   dz_t     = dy_t * ypre_t * SiLU'(z_t)
- *   lambda_t = dh_t (total adjoint of h_t)
- *            = C_t dypre_t + A_bar_{t+1} lambda_{t+1}   (lambda_L-1 gets + dh_last)
- *   dB_t[n] += lambda_t[n] Delta_t u_t                    (summed over channels)
- *   dC_t[n] += dypre_t h_t[n]                             (summed over channels)
- *   du_t     = dypre_t D + Delta_t sum_n lambda_t[n] B_t[n]
- *   dDelta_t = sum_n lambda_t[n] (A[n] A_bar_t[n] h_{t-1}[n] + B_t[n] u_t)
- *   dA[n]   += lambda_t[n] Delta_t A_bar_t[n] h_{t-1}[n]  (summed over batch, t)
- *   dD      += dypre_t u_t
- *   ddelta_t = dDelta_t * sigmoid(Delta_raw + bias)  (softplus; else dDelta_t)
- *   dbias   += ddelta_t
- *   dh0      = A_bar_0 lambda_0
+ * states are recomputed, here simply by a stored forward loop).  In scan
+ * order s (s = t, or t = L-1-s for ORACLE_REVERSE), with the B_bar
+ * coefficient c_n(Delta, a_n) (Delta, or expm1(Delta a_n)/a_n for exact ZOH),
+ * ypre = sum_n C[n] h[n] + D u and y = ypre * SiLU(z):
+ *   dypre    = dy * SiLU(z)
+ *   dz       = dy * ypre * SiLU'(z)
+ *   lambda_s = dh_s (total adjoint of h_s)
+ *            = C_s dypre_s + A_bar_{s+1} lambda_{s+1}   (lambda of the last step gets + dh_last)
+ *   dB[n]   += lambda[n] c_n u                            (summed over channels)
+ *   dC[n]   += dypre h_s[n]                               (summed over channels)
+ *   du_s     = dypre D + sum_n lambda[n] c_n B[n]         (u: the scan input)
+ *   dDelta_s = sum_n lambda[n] (a_n A_bar[n] h_{s-1}[n] + dc_n/dDelta B[n] u)
+ *   dA[n]   += lambda[n] (Delta A_bar[n] h_{s-1}[n] + dc_n/da_n B[n] u)
+ *   dD      += dypre u
+ *   ddelta   = dDelta * sigmoid(Delta_raw + bias)  (softplus; else dDelta)
+ *   dbias   += ddelta
+ *   dh0      = A_bar_0 lambda_0                           (the first scan step)
+ * With the conv prologue, u_s = SiLU(acc_s), acc_s = cb + sum_j w_j x_{s-k+1+j}
+ * (scan order), and the gradient flows on to the raw input x and the taps:
+ *   g_s = du_s SiLU'(acc_s);  dx_{s-k+1+j} += w_j g_s;  dw_j += g_s x_{s-k+1+j};  dcb += g_s.
  *
- * Inputs as oracle_fwd, plus dy (batch, L, dim) fp32 and dh_last
- * (batch, dim, N) double or NULL.  Outputs (all double, all written):
- * du, ddelta, dz (batch, L, dim) (dz only when z is given), dA (dim, N),
- * dB, dC (batch, L, N), dD, dbias (dim), dh0 (batch, dim, N).
+ * Inputs as oracle_fwd_ex, plus dy (batch, L, dim) fp32 and dh_last
+ * (batch, dim, N) double or NULL.  Outputs (all double, all written): du
+ * (the gradient of u, the raw input of the conv prologue when there is one),
+ * ddelta, dz (batch, L, dim) (dz only when z is given), dA (dim, N), dB, dC
+ * (batch, L, N), dD, dbias (dim), dh0 (batch, dim, N), and with conv_w
+ * dconv_w (dim, conv_k) and dconv_b (dim).
  * Threads split the channels; dB and dC are summed from per-thread buffers.
  */
-int oracle_bwd(const float *u, const float *delta, const float *A,
-               const float *Bm, const float *Cm, const float *D_skip,
-               const float *z, const float *delta_bias, int delta_softplus,
-               const double *h0, const float *dy, const double *dh_last,
-               double *du, double *ddelta, double *dA, double *dB, double *dC,
-               double *dD, double *dz, double *dbias, double *dh0,
-               int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads)
+int oracle_bwd_ex(const float *u, const float *delta, const float *A,
+                  const float *Bm, const float *Cm, const float *D_skip,
+                  const float *z, const float *delta_bias, int delta_softplus,
+                  const double *h0, const float *dy, const double *dh_last,
+                  double *du, double *ddelta, double *dA, double *dB, double *dC,
+                  double *dD, double *dz, double *dbias, double *dh0,
+                  int64_t batch, int64_t L, int64_t dim, int64_t N, int flags,
+                  const float *conv_w, const float *conv_b, int64_t conv_k,
+                  double *dconv_w, double *dconv_b, int nthreads)
 {
-    if (batch < 1 || L < 1 || dim < 1 || N < 1)
+    if (batch < 1 || L < 1 || dim < 1 || N < 1 || (conv_w && conv_k < 1))
         return 1;
     if (nthreads > 0)
         omp_set_num_threads(nthreads);
+    const int zoh = (flags & ORACLE_ZOH_EXACT) != 0;
+    const int rev = (flags & ORACLE_REVERSE) != 0;
     const int64_t bln = batch * L * N;
     int nth = 1;
 #pragma omp parallel
@@ -277,8 +307,12 @@ int oracle_bwd(const float *u, const float *delta, const float *A,
         double *myB = accB + (size_t)tid * bln;
         double *myC = accC + (size_t)tid * bln;
         double *hs = (double *)malloc((size_t)(L + 1) * N * sizeof(double));
+        double *us = (double *)malloc((size_t)L * sizeof(double));   /* scan input, scan order */
+        double *as = (double *)malloc((size_t)L * sizeof(double));   /* conv pre-activation */
+        double *xs = (double *)malloc((size_t)L * sizeof(double));   /* raw input, scan order */
+        double *gs = (double *)malloc((size_t)L * sizeof(double));   /* d/d(scan input) */
         double *lam = (double *)malloc((size_t)N * sizeof(double));
-        if (!hs || !lam) {
+        if (!hs || !us || !as || !xs || !gs || !lam) {
 #pragma omp atomic write
             bad = 1;
         } else {
@@ -287,31 +321,58 @@ int oracle_bwd(const float *u, const float *delta, const float *A,
                 double sD = 0.0, sbias = 0.0;
                 for (int64_t n = 0; n < N; ++n)
                     dA[d * N + n] = 0.0;
+                if (conv_w) {
+                    for (int64_t j = 0; j < conv_k; ++j)
+                        dconv_w[d * conv_k + j] = 0.0;
+                    dconv_b[d] = 0.0;
+                }
                 const double Dd = D_skip ? (double)D_skip[d] : 0.0;
                 for (int64_t b = 0; b < batch; ++b) {
-                    /* forward, keeping every state: hs[t+1] = h_t, hs[0] = h0 */
+                    /* scan-order inputs and the conv prologue */
+                    for (int64_t s = 0; s < L; ++s) {
+                        int64_t t = rev ? L - 1 - s : s;
+                        xs[s] = (double)u[(b * L + t) * dim + d];
+                    }
+                    for (int64_t s = 0; s < L; ++s) {
+                        if (conv_w) {
+                            double acc = conv_b ? (double)conv_b[d] : 0.0;
+                            for (int64_t j = 0; j < conv_k; ++j) {
+                                int64_t ss = s - (conv_k - 1) + j;
+                                if (ss >= 0)
+                                    acc += (double)conv_w[d * conv_k + j] * xs[ss];
+                            }
+                            as[s] = acc;
+                            us[s] = silu(acc);
+                        } else {
+                            us[s] = xs[s];
+                        }
+                    }
+                    /* forward, keeping every state: hs[s+1] = h after scan step s */
                     for (int64_t n = 0; n < N; ++n)
                         hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
-                    for (int64_t t = 0; t < L; ++t) {
+                    for (int64_t s = 0; s < L; ++s) {
+                        int64_t t = rev ? L - 1 - s : s;
                         int64_t e = (b * L + t) * dim + d;
                         const float *Bt = Bm + (b * L + t) * N;
                         double dt = step_delta((double)delta[e], delta_bias, d, delta_softplus);
-                        double ut = (double)u[e];
-                        for (int64_t n = 0; n < N; ++n)
-                            hs[(t + 1) * N + n] = exp(dt * (double)A[d * N + n]) * hs[t * N + n] +
-                                                  dt * (double)Bt[n] * ut;
+                        for (int64_t n = 0; n < N; ++n) {
+                            double an = (double)A[d * N + n];
+                            hs[(s + 1) * N + n] = exp(dt * an) * hs[s * N + n] +
+                                                  bbar_coeff(dt, an, zoh) * (double)Bt[n] * us[s];
+                        }
                     }
-                    /* backward */
+                    /* backward, in reverse scan order */
                     for (int64_t n = 0; n < N; ++n)
                         lam[n] = dh_last ? dh_last[(b * dim + d) * N + n] : 0.0;
-                    for (int64_t t = L - 1; t >= 0; --t) {
+                    for (int64_t s = L - 1; s >= 0; --s) {
+                        int64_t t = rev ? L - 1 - s : s;
                         int64_t e = (b * L + t) * dim + d;
                         const float *Bt = Bm + (b * L + t) * N;
                         const float *Ct = Cm + (b * L + t) * N;
                         double x = (double)delta[e] + (delta_bias ? (double)delta_bias[d] : 0.0);
                         double dt = delta_softplus ? softplus(x) : x;
-                        double ut = (double)u[e];
-                        const double *ht = hs + (t + 1) * N, *hp = hs + t * N;
+                        double ut = us[s];
+                        const double *ht = hs + (s + 1) * N, *hp = hs + s * N;
                         double ypre = Dd * ut;
                         for (int64_t n = 0; n < N; ++n)
                             ypre += (double)Ct[n] * ht[n];
@@ -322,22 +383,25 @@ int oracle_bwd(const float *u, const float *delta, const float *A,
                             dypre = dyt * zt * sg;
                             dz[e] = dyt * ypre * sg * (1.0 + zt * (1.0 - sg));
                         }
-                        double sLB = 0.0, dDelta = 0.0;
+                        double sLcB = 0.0, dDelta = 0.0;
                         for (int64_t n = 0; n < N; ++n) {
                             double an = (double)A[d * N + n];
                             double abar = exp(dt * an);
-                            /* lam holds the adjoint arriving from t+1 (already
-                               multiplied by A_bar_{t+1}); add this step's readout */
+                            double cn = bbar_coeff(dt, an, zoh);
+                            /* lam holds the adjoint arriving from the next scan
+                               step (already multiplied by its A_bar); add this
+                               step's readout */
                             double l = lam[n] + (double)Ct[n] * dypre;
                             myC[(b * L + t) * N + n] += dypre * ht[n];
-                            myB[(b * L + t) * N + n] += l * dt * ut;
-                            sLB += l * (double)Bt[n];
-                            dDelta += l * an * abar * hp[n];
-                            dA[d * N + n] += l * dt * abar * hp[n];
+                            myB[(b * L + t) * N + n] += l * cn * ut;
+                            sLcB += l * cn * (double)Bt[n];
+                            dDelta += l * (an * abar * hp[n] +
+                                           bbar_coeff_ddt(dt, an, zoh) * (double)Bt[n] * ut);
+                            dA[d * N + n] += l * (dt * abar * hp[n] +
+                                                  bbar_coeff_da(dt, an, zoh) * (double)Bt[n] * ut);
                             lam[n] = abar * l;
                         }
-                        dDelta += sLB * ut;
-                        du[e] = dypre * Dd + dt * sLB;
+                        gs[s] = dypre * Dd + sLcB;            /* gradient of the scan input */
                         double ddl = delta_softplus ? dDelta / (1.0 + exp(-x)) : dDelta;
                         ddelta[e] = ddl;
                         sbias += ddl;
@@ -345,12 +409,36 @@ int oracle_bwd(const float *u, const float *delta, const float *A,
                     }
                     for (int64_t n = 0; n < N; ++n)
                         dh0[(b * dim + d) * N + n] = lam[n];
+                    /* through the conv prologue to the raw input and the taps */
+                    for (int64_t s = 0; s < L; ++s) {
+                        int64_t t = rev ? L - 1 - s : s;
+                        du[(b * L + t) * dim + d] = conv_w ? 0.0 : gs[s];
+                    }
+                    if (conv_w) {
+                        for (int64_t s = 0; s < L; ++s) {
+                            double sg = 1.0 / (1.0 + exp(-as[s]));
+                            double g = gs[s] * sg * (1.0 + as[s] * (1.0 - sg));
+                            dconv_b[d] += g;
+                            for (int64_t j = 0; j < conv_k; ++j) {
+                                int64_t ss = s - (conv_k - 1) + j;
+                                if (ss < 0)
+                                    continue;
+                                int64_t tt = rev ? L - 1 - ss : ss;
+                                du[(b * L + tt) * dim + d] += (double)conv_w[d * conv_k + j] * g;
+                                dconv_w[d * conv_k + j] += g * xs[ss];
+                            }
+                        }
+                    }
                 }
                 dD[d] = sD;
                 dbias[d] = sbias;
             }
         }
         free(hs);
+        free(us);
+        free(as);
+        free(xs);
+        free(gs);
         free(lam);
     }
     if (!bad) {
@@ -367,4 +455,17 @@ int oracle_bwd(const float *u, const float *delta, const float *A,
     free(accB);
     free(accC);
     return bad ? 2 : 0;
+}
+
+int oracle_bwd(const float *u, const float *delta, const float *A,
+               const float *Bm, const float *Cm, const float *D_skip,
+               const float *z, const float *delta_bias, int delta_softplus,
+               const double *h0, const float *dy, const double *dh_last,
+               double *du, double *ddelta, double *dA, double *dB, double *dC,
+               double *dD, double *dz, double *dbias, double *dh0,
+               int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads)
+{
+    return oracle_bwd_ex(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, dy,
+                         dh_last, du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch, L, dim, N, 0,
+                         NULL, NULL, 0, NULL, NULL, nthreads);
 }
