@@ -5,6 +5,7 @@
     python bench.py --parse-pmc FETCH_DIR WRITE_DIR   # -> profiles/traffic_<workload>.json
     python bench.py --pass bwd           # the backward (selscan_bwd) on the same workload
     python bench.py --variant zoh,rev,conv4   # forward variants through selscan_fwd_ex
+    python bench.py --pass bwd --variant zoh,rev,conv4   # their backward (selscan_bwd_ex)
 
 One step = one selscan_fwd call over one batch of the workload.  The default
 workload is one Mamba-130M layer: batch 8, L 2048, D 1536, N 16, bf16 inputs,
@@ -308,8 +309,18 @@ def bench_bwd(w, args):
     ws = torch.empty(ss.selscan_bwd_workspace_bytes(w.batch, w.L, w.dim, w.N, code),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    vflags, vconv = parse_variant(args.variant)
+    conv_w = conv_b = None
+    if vconv:
+        cw, cb = si.conv_params(w.dim, vconv, w.seed)
+        conv_w, conv_b = torch.from_numpy(cw).to(dev), torch.from_numpy(cb).to(dev)
 
     def step():
+        if args.variant:
+            ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"],
+                              t["z"], t["delta_bias"], True, None, None, flags=vflags,
+                              conv_weight=conv_w, conv_bias=conv_b, workspace=ws, stream=stream)
+            return
         ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"], t["z"],
                        t["delta_bias"], True, None, None, workspace=ws, stream=stream)
 
@@ -351,6 +362,10 @@ def bench_bwd(w, args):
                      "algorithmic_bytes_per_call": nb,
                      "hbm_gbps_of_call": nb / (call_mean * 1e-3) / 1e9},
     }
+    if args.variant:
+        res["variant"] = args.variant
+        res["roofline"]["kernel"] = "selscan_bwd_ex call (%s); slots of the default path" \
+            % args.variant
     print(json.dumps(res), flush=True)
 
 
@@ -379,7 +394,7 @@ def main():
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
-    ap.add_argument("--variant", default="", help="forward variants: zoh, rev, convK")
+    ap.add_argument("--variant", default="", help="variants: zoh, rev, convK (fwd or bwd)")
     args = ap.parse_args()
 
     import selscan_inputs as si

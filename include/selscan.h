@@ -32,6 +32,9 @@
  *                        deep-reading report §2.4 (recomputation in the backward
  *                        pass), selection-mechanism article (discosf.com) §3.4.
  *
+ *  selscan_bwd_ex        gradients of selscan_fwd_ex (the variants above), and of
+ *                        the conv prologue's taps and bias.
+ *
  *  selscan_state_update  one decode step of the same recurrence on a resident
  *                        state: constant memory and O(1) work per token, one
  *                        state per sample.  Sources: Mamba tutorial §5.1 table
@@ -84,7 +87,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 3
+#define SELSCAN_ABI_VERSION 4
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -201,6 +204,7 @@ int selscan_fwd_ex(const void *u, const void *delta, const float *A,
  * forward and of the adjoint, the recomputation checkpoints (the state at the
  * start of every 4-step chunk: batch * ceil(dim/64) * ceil(L/4) * N * 256
  * bytes) and the partial sums of the reduced gradients.  No initialisation.
+ * The same size serves selscan_bwd_ex, with or without the conv prologue.
  */
 size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype);
 
@@ -245,6 +249,40 @@ int selscan_bwd(const void *u, const void *delta, const float *A,
                 float *dD, void *dz, float *ddelta_bias, float *dh0,
                 int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of selscan_fwd_ex: the gradient of
+ *     sum(dy * y) + sum(dh_last * h_last)
+ * for the forward that selscan_fwd_ex computes with the same flags and conv
+ * prologue.  Arguments as selscan_bwd, plus flags, conv_weight, conv_bias and
+ * conv_width as selscan_fwd_ex, and:
+ *   dconv_weight  (dim, conv_width) fp32  written; required when conv_width > 0
+ *   dconv_bias    (dim)             fp32  written; NULL to skip (defined even
+ *                                         when conv_bias is NULL)
+ * Both are ignored when conv_width = 0.  With the conv prologue, du is the
+ * gradient of the raw input u (the conv's input).  With REVERSE, h0 and dh0
+ * belong to the state entering t = L-1, dh_last to the state after t = 0.
+ * With ZOH_EXACT, the B_bar coefficient c = (exp(Delta A) - 1) / A replaces
+ * Delta in du, dB and the dDelta, dA terms of B_bar: dc/dDelta = exp(Delta A),
+ * dc/dA = (Delta exp(Delta A) - c) / A (Delta^2 / 2 where A = 0).
+ * Sources: as selscan_fwd_ex for the forward; the gradients are its exact
+ * derivatives (the recomputation as for selscan_bwd).
+ *
+ * Workspace: selscan_bwd_workspace_bytes.  dconv_weight and dconv_bias are
+ * sums in a fixed order (bitwise repeatable) like dA.  Errors as selscan_bwd
+ * and selscan_fwd_ex, and SELSCAN_ERR_NULL for conv_width > 0 without
+ * dconv_weight.
+ */
+int selscan_bwd_ex(const void *u, const void *delta, const float *A,
+                   const void *Bm, const void *Cm, const float *D_skip,
+                   const void *z, const float *delta_bias, int delta_softplus,
+                   const float *h0, const void *dy, const float *dh_last,
+                   void *du, void *ddelta, float *dA, float *dB, float *dC,
+                   float *dD, void *dz, float *ddelta_bias, float *dh0,
+                   int flags, const float *conv_weight, const float *conv_bias,
+                   int64_t conv_width, float *dconv_weight, float *dconv_bias,
+                   int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
+                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step, updating `state` in place:

@@ -11,6 +11,7 @@ is no CPU fallback.  If ``libselscan.so`` is missing, every call raises.
                        conv_weight=w, conv_bias=b)
     grads = selscan_bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, h0=h0,
                         dh_last=dh_last)
+    grads = selscan_bwd_ex(..., flags=..., conv_weight=w, conv_bias=b)
     y = selscan_state_update(state, u, delta, A, Bm, Cm, D_skip, z, delta_bias)
 """
 from ._abi import (  # noqa: F401
@@ -23,6 +24,7 @@ from ._abi import (  # noqa: F401
     lib,
     lib_path,
     selscan_bwd,
+    selscan_bwd_ex,
     selscan_bwd_workspace_bytes,
     selscan_fwd,
     selscan_fwd_ex,

@@ -68,6 +68,10 @@ def lib():
         L.selscan_bwd.argtypes = [P] * 12 + [P] * 9 + [I64, I64, I64, I64, I, P,
                                                       ctypes.c_size_t, P]
         L.selscan_bwd.argtypes[8] = I
+        L.selscan_bwd_ex.restype = I
+        L.selscan_bwd_ex.argtypes = [P] * 12 + [P] * 9 + [I, P, P, I64, P, P] + \
+            [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+        L.selscan_bwd_ex.argtypes[8] = I
         L.selscan_state_update.restype = I
         L.selscan_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
         _lib = L
@@ -220,6 +224,29 @@ def selscan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch
     stream).  dy: (batch, L, dim) in the input dtype; dh_last: (batch, dim, N)
     float32 or None.  Returns a dict with du, ddelta, dz (None without z) in the
     input dtype and dA, dB, dC, dD, ddelta_bias, dh0 in float32."""
+    return _bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, delta_softplus, h0, dh_last,
+                workspace, stream, None)
+
+
+def selscan_bwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                   Cm: torch.Tensor, dy: torch.Tensor, D_skip: Optional[torch.Tensor] = None,
+                   z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                   delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                   dh_last: Optional[torch.Tensor] = None, flags: int = 0,
+                   conv_weight: Optional[torch.Tensor] = None,
+                   conv_bias: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> dict:
+    """Gradients of ``selscan_fwd_ex`` (same ``flags``, ``conv_weight``,
+    ``conv_bias``) through ``selscan_bwd_ex``.  The dict of ``selscan_bwd``,
+    plus dconv_weight (dim, k) and dconv_bias (dim,) in float32 with the conv
+    prologue (None without); du is then the gradient of the conv's input u."""
+    return _bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, delta_softplus, h0, dh_last,
+                workspace, stream, (int(flags), conv_weight, conv_bias))
+
+
+def _bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, delta_softplus, h0, dh_last, workspace,
+         stream, ex):
     L_ = lib()
     dev = u.device
     dt = u.dtype
@@ -250,15 +277,34 @@ def selscan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch
     ws_bytes = int(L_.selscan_bwd_workspace_bytes(batch, L, dim, N, code))
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    rc = L_.selscan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
-                        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy),
-                        _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
-                        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-                        _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, L, dim, N, code,
-                        _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        _stream(dev, stream))
+    common = (_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
+              _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dh_last),
+              _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+              _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]))
+    tail = (batch, L, dim, N, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(dev, stream))
+    if ex is None:
+        name = "selscan_bwd"
+        rc = L_.selscan_bwd(*common, *tail)
+    else:
+        name = "selscan_bwd_ex"
+        flags, conv_weight, conv_bias = ex
+        k = 0
+        g["dconv_weight"] = g["dconv_bias"] = None
+        if conv_weight is not None:
+            if conv_weight.dim() != 2:
+                raise ValueError("conv_weight must be (dim, k), got %s" % (tuple(conv_weight.shape),))
+            k = conv_weight.shape[1]
+            conv_weight = _prep(conv_weight, f32, dev, "conv_weight", (dim, k))
+            conv_bias = _prep(conv_bias, f32, dev, "conv_bias", (dim,))
+            g["dconv_weight"] = torch.empty((dim, k), dtype=f32, device=dev)
+            g["dconv_bias"] = torch.empty((dim,), dtype=f32, device=dev)
+        elif conv_bias is not None:
+            raise ValueError("conv_bias given without conv_weight")
+        rc = L_.selscan_bwd_ex(*common, flags, _ptr(conv_weight), _ptr(conv_bias), k,
+                               _ptr(g["dconv_weight"]), _ptr(g["dconv_bias"]), *tail)
     if rc != 0:
-        raise SelscanError(rc, "selscan_bwd", L_.selscan_last_hip_error())
+        raise SelscanError(rc, name, L_.selscan_last_hip_error())
     return g
 
 

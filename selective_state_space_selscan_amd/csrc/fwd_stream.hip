@@ -117,6 +117,25 @@ hipError_t launch_fwd_summaries(const FwdArgs &a, const StreamPlan &p, float *su
                         : summaries_t<float>(a, p, summ, stream);
 }
 
+hipError_t launch_fwd_summaries_ext(const FwdArgs &a, const FwdExt &e, const StreamPlan &p,
+                                   float *summ, hipStream_t stream)
+{
+    const bool zoh = (e.flags & kFwdFlagZohExact) != 0;
+#define SELSCAN_EXT_CASE(NN)                                                                      \
+    case NN:                                                                                      \
+        return zoh ? launch_fwd_summaries_ext_n##NN##_zoh(a, e, p, summ, stream)                  \
+                   : launch_fwd_summaries_ext_n##NN(a, e, p, summ, stream);
+    switch (a.N) {
+    SELSCAN_EXT_CASE(4)
+    SELSCAN_EXT_CASE(8)
+    SELSCAN_EXT_CASE(16)
+    SELSCAN_EXT_CASE(32)
+    SELSCAN_EXT_CASE(64)
+    default: return hipErrorInvalidValue;
+    }
+#undef SELSCAN_EXT_CASE
+}
+
 hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream)
 {
     const bool zoh = (e.flags & kFwdFlagZohExact) != 0;

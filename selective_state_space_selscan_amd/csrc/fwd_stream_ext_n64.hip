@@ -11,4 +11,10 @@ hipError_t launch_fwd_stream_ext_n64(const FwdArgs &a, const FwdExt &e, hipStrea
     return stream::launch_ext<64, false>(a, e, stream);
 }
 
+hipError_t launch_fwd_summaries_ext_n64(const FwdArgs &a, const FwdExt &e, const StreamPlan &p,
+                                        float *summ, hipStream_t stream)
+{
+    return stream::launch_ext_summaries<64, false>(a, e, p, summ, stream);
+}
+
 } // namespace selscan

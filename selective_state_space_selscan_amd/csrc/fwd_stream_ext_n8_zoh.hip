@@ -11,4 +11,10 @@ hipError_t launch_fwd_stream_ext_n8_zoh(const FwdArgs &a, const FwdExt &e, hipSt
     return stream::launch_ext<8, true>(a, e, stream);
 }
 
+hipError_t launch_fwd_summaries_ext_n8_zoh(const FwdArgs &a, const FwdExt &e, const StreamPlan &p,
+                                        float *summ, hipStream_t stream)
+{
+    return stream::launch_ext_summaries<8, true>(a, e, p, summ, stream);
+}
+
 } // namespace selscan

@@ -448,6 +448,31 @@ __device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta,
     }
 }
 
+// Conv prologue taps of channel d, aligned to the newest input (zeros in
+// front when conv_k < kMaxConv), and the conv bias.
+__device__ __forceinline__ void conv_taps(WaveCtx &c, const ExtParams &ext, int64_t d)
+{
+#pragma unroll
+    for (int m = 0; m < kMaxConv; ++m) {
+        const int j = m - (kMaxConv - ext.conv_k);
+        c.cw[m] = j >= 0 ? ext.conv_w[d * ext.conv_k + j] : 0.0f;
+    }
+    c.cb = ext.conv_b ? ext.conv_b[d] : 0.0f;
+}
+
+// Raw inputs of the kMaxConv - 1 scan steps before the part, oldest first
+// (zero before scan step 0).
+template <int VAR, typename TIO>
+__device__ __forceinline__ void conv_window(float (&win)[kMaxConv - 1], const WaveCtx &c,
+                                            const TIO *u, int64_t d)
+{
+#pragma unroll
+    for (int j = 0; j < kMaxConv - 1; ++j) {
+        const int64_t s = c.l_begin - (kMaxConv - 1) + j;
+        win[j] = s >= 0 ? load_elem(u, scan_row<VAR>(c, s) * c.dim + d) : 0.0f;
+    }
+}
+
 // h <- exp(A S) h + x for one part summary v = (S, x[0..N-1]); for structured
 // A, exp(A[d,n] S) = e^(n+1) with e = exp(A[d,0] S).
 constexpr int kFoldGroup = 4;
@@ -573,25 +598,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
     c.bias = delta_bias ? delta_bias[d] : 0.0f;
     c.Dd = (!SUMMARY && D_skip) ? D_skip[d] : 0.0f;
 
-    // Conv prologue: taps aligned to the newest input (zeros in front when
-    // conv_k < kMaxConv), and the raw inputs of the steps before the part.
+    // Conv prologue: taps, and the raw inputs of the steps before the part.
     float win[kMaxConv - 1];
 #pragma unroll
     for (int j = 0; j < kMaxConv - 1; ++j)
         win[j] = 0.0f;
     if constexpr (CONV) {
-#pragma unroll
-        for (int m = 0; m < kMaxConv; ++m) {
-            const int j = m - (kMaxConv - ext.conv_k);
-            c.cw[m] = j >= 0 ? ext.conv_w[d * ext.conv_k + j] : 0.0f;
-        }
-        c.cb = ext.conv_b ? ext.conv_b[d] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < kMaxConv - 1; ++j) {
-            const int64_t s = c.l_begin - (kMaxConv - 1) + j;
-            if (s >= 0)
-                win[j] = load_elem(u, scan_row<VAR>(c, s) * dim + d);
-        }
+        conv_taps(c, ext, d);
+        conv_window<VAR>(win, c, u, d);
     }
 
     // Entry state: zero for a summary; for the main pass h0 (or zero) carried
@@ -669,6 +683,37 @@ hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p,
                        (const TIO *)a.z, (TIO *)a.y, a.A, (const TIO *)a.Bm, (const TIO *)a.Cm,
                        a.D_skip, a.delta_bias, a.delta_softplus, a.h0, a.h_last, summ, a.L,
                        a.dim, p.groups, p.parts, p.part_len, ext);
+    return hipGetLastError();
+}
+
+// Summary pass alone of a variant forward, for a given plan (the backward's).
+template <int N, bool ZOH>
+hipError_t launch_ext_summaries(const FwdArgs &a, const FwdExt &e, const StreamPlan &p,
+                                float *summ, hipStream_t s)
+{
+    const int64_t waves = p.groups * (p.parts - 1);
+    if (waves <= 0)
+        return hipSuccess;
+    ExtParams x;
+    x.conv_w = e.conv_k > 0 ? e.conv_w : nullptr;
+    x.conv_b = e.conv_k > 0 ? e.conv_b : nullptr;
+    x.conv_k = e.conv_k;
+    x.rev = (e.flags & kFwdFlagReverse) ? 1 : 0;
+    constexpr int V = kVarExt | (ZOH ? kVarZoh : 0);
+    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 block(kLanes * kWavesPerBlock);
+#define SELSCAN_SUMM(VV, T)                                                                       \
+    hipLaunchKernelGGL((fwd_stream_kernel<N, true, VV, T>), grid, block, 0, s, (const T *)a.u,     \
+                       (const T *)a.delta, (const T *)nullptr, (T *)nullptr, a.A,                 \
+                       (const T *)a.Bm, (const T *)a.Cm, (const float *)nullptr, a.delta_bias,   \
+                       a.delta_softplus, (const float *)nullptr, (float *)nullptr, summ, a.L,     \
+                       a.dim, p.groups, p.parts, p.part_len, x)
+    if (a.dtype == 1) {
+        if (e.conv_k > 0) SELSCAN_SUMM(V | kVarConv, uint16_t); else SELSCAN_SUMM(V, uint16_t);
+    } else {
+        if (e.conv_k > 0) SELSCAN_SUMM(V | kVarConv, float); else SELSCAN_SUMM(V, float);
+    }
+#undef SELSCAN_SUMM
     return hipGetLastError();
 }
 

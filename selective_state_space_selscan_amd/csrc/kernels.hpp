@@ -80,7 +80,11 @@ hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t 
 // One translation unit per (N, B_bar form): fwd_stream_ext_n<N>[_zoh].hip.
 #define SELSCAN_DECLARE_EXT(NN)                                                                   \
     hipError_t launch_fwd_stream_ext_n##NN(const FwdArgs &a, const FwdExt &e, hipStream_t s);    \
-    hipError_t launch_fwd_stream_ext_n##NN##_zoh(const FwdArgs &a, const FwdExt &e, hipStream_t s);
+    hipError_t launch_fwd_stream_ext_n##NN##_zoh(const FwdArgs &a, const FwdExt &e, hipStream_t s); \
+    hipError_t launch_fwd_summaries_ext_n##NN(const FwdArgs &a, const FwdExt &e,                 \
+                                              const StreamPlan &p, float *summ, hipStream_t s);  \
+    hipError_t launch_fwd_summaries_ext_n##NN##_zoh(const FwdArgs &a, const FwdExt &e,           \
+                                                    const StreamPlan &p, float *summ, hipStream_t s);
 SELSCAN_DECLARE_EXT(4)
 SELSCAN_DECLARE_EXT(8)
 SELSCAN_DECLARE_EXT(16)
@@ -92,10 +96,13 @@ SELSCAN_DECLARE_EXT(64)
 // default instantiation) into summ: (groups, parts - 1, N + 1, 64) fp32.
 hipError_t launch_fwd_summaries(const FwdArgs &a, const StreamPlan &p, float *summ,
                                 hipStream_t stream);
+// The same for a variant forward.
+hipError_t launch_fwd_summaries_ext(const FwdArgs &a, const FwdExt &e, const StreamPlan &p,
+                                   float *summ, hipStream_t stream);
 
-// Backward (gradients of the default forward).  `fwd` carries the forward's
-// inputs, dtype, sizes and the workspace; y, h_last, h0-independent fields of
-// it are unused.
+// Backward (gradients of the default forward, or of a variant forward).
+// `fwd` carries the forward's inputs, dtype, sizes and the workspace; its y
+// and h_last are unused.
 struct BwdArgs {
     FwdArgs fwd;
     const void *dy;         // (batch, L, dim) dtype
@@ -105,9 +112,18 @@ struct BwdArgs {
     float *dB, *dC;         // (batch, L, N)
     float *dD, *ddelta_bias;// (dim) or null
     float *dh0;             // (batch, dim, N) or null
+    float *dconv_w;         // (dim, conv_k): with the conv prologue only
+    float *dconv_b;         // (dim) or null: with the conv prologue only
 };
 size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
-hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+// e: the variant (null or flags 0 without conv: the default forward).
+hipError_t launch_bwd(const BwdArgs &a, const FwdExt *e, hipStream_t stream);
+// One translation unit per variant: bwd_stream[_rev|_zoh|_conv|_zoh_conv].hip.
+hipError_t launch_bwd_euler(const BwdArgs &a, const FwdExt &e, hipStream_t stream);
+hipError_t launch_bwd_euler_rev(const BwdArgs &a, const FwdExt &e, hipStream_t stream);
+hipError_t launch_bwd_zoh(const BwdArgs &a, const FwdExt &e, hipStream_t stream);
+hipError_t launch_bwd_euler_conv(const BwdArgs &a, const FwdExt &e, hipStream_t stream);
+hipError_t launch_bwd_zoh_conv(const BwdArgs &a, const FwdExt &e, hipStream_t stream);
 
 // Decode step.
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);

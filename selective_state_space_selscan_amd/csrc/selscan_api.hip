@@ -150,6 +150,78 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
     }
 }
 
+// Shared by selscan_bwd (ext == NULL) and selscan_bwd_ex.
+int bwd_common(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+               const float *D_skip, const void *z, const float *delta_bias, int delta_softplus,
+               const float *h0, const void *dy, const float *dh_last, void *du, void *ddelta,
+               float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
+               float *dh0, const selscan::FwdExt *ext, float *dconv_w, float *dconv_b,
+               int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype, void *workspace,
+               size_t workspace_bytes, void *stream)
+{
+    if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
+        return SELSCAN_ERR_DTYPE;
+    const int64_t elems = checked_count(batch, L, dim);
+    const int64_t bcn = checked_count(batch, L, N > 0 ? N : 1);
+    const int64_t states = checked_count(batch, dim, N > 0 ? N : 1);
+    if (elems < 0 || bcn < 0 || states < 0 || N < 1)
+        return SELSCAN_ERR_SHAPE;
+    if (!u || !delta || !A || !Bm || !Cm || !dy || !du || !ddelta || !dA || !dB || !dC ||
+        (z && !dz))
+        return SELSCAN_ERR_NULL;
+    if (!supported_n(N) || dim > kMaxDim)
+        return SELSCAN_ERR_UNSUPPORTED;
+    if (!z)
+        dz = nullptr;
+    const int64_t conv_k = ext ? ext->conv_k : 0;
+    const float *conv_w = conv_k > 0 ? ext->conv_w : nullptr;
+    const float *conv_b = conv_k > 0 ? ext->conv_b : nullptr;
+    if (conv_k > 0 && (!conv_w || !dconv_w))
+        return SELSCAN_ERR_NULL;
+    if (conv_k == 0)
+        dconv_w = dconv_b = nullptr;
+    const void *all[] = {u,  delta, A,  Bm, Cm, D_skip, z,  delta_bias,  h0,  dy,       dh_last,
+                         du, ddelta, dA, dB, dC, dD,     dz, ddelta_bias, dh0, workspace,
+                         conv_w, conv_b, dconv_w, dconv_b};
+    for (const void *p : all)
+        if (p && !aligned16(p))
+            return SELSCAN_ERR_UNSUPPORTED;
+    const size_t need = selscan_bwd_workspace_bytes(batch, L, dim, N, dtype);
+    if (!workspace || workspace_bytes < need)
+        return SELSCAN_ERR_WORKSPACE;
+
+    const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
+    const Range ins[] = {{u, elems * es},       {delta, elems * es},   {A, dim * N * 4},
+                         {Bm, bcn * es},        {Cm, bcn * es},        {D_skip, dim * 4},
+                         {z, elems * es},       {delta_bias, dim * 4}, {h0, states * 4},
+                         {dy, elems * es},      {dh_last, states * 4}, {workspace, (int64_t)need},
+                         {conv_w, dim * conv_k * 4}, {conv_b, dim * 4}};
+    const Range outs[] = {{du, elems * es}, {ddelta, elems * es}, {dA, dim * N * 4},
+                          {dB, bcn * 4},    {dC, bcn * 4},        {dD, dim * 4},
+                          {dz, elems * es}, {ddelta_bias, dim * 4}, {dh0, states * 4},
+                          {dconv_w, dim * conv_k * 4}, {dconv_b, dim * 4}};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return SELSCAN_ERR_ALIAS;
+    const int n_out = (int)(sizeof(outs) / sizeof(outs[0]));
+    for (int i = 0; i < n_out; ++i)
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return SELSCAN_ERR_ALIAS;
+
+    selscan::BwdArgs a;
+    selscan::FwdArgs &f = a.fwd;
+    f.u = u; f.delta = delta; f.A = A; f.Bm = Bm; f.Cm = Cm; f.D_skip = D_skip; f.z = z;
+    f.delta_bias = delta_bias; f.delta_softplus = delta_softplus ? 1 : 0; f.h0 = h0;
+    f.y = nullptr; f.h_last = nullptr; f.batch = batch; f.L = L; f.dim = dim; f.N = N;
+    f.dtype = dtype; f.workspace = workspace; f.workspace_bytes = workspace_bytes;
+    a.dy = dy; a.dh_last = dh_last; a.du = du; a.ddelta = ddelta; a.dz = dz; a.dA = dA;
+    a.dB = dB; a.dC = dC; a.dD = dD; a.ddelta_bias = ddelta_bias; a.dh0 = dh0;
+    a.dconv_w = dconv_w; a.dconv_b = dconv_b;
+    return finish_launch(selscan::launch_bwd(a, ext, (hipStream_t)stream));
+}
+
 } // namespace
 
 extern "C" {
@@ -234,56 +306,35 @@ int selscan_bwd(const void *u, const void *delta, const float *A, const void *Bm
                 float *dh0, int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
-        return SELSCAN_ERR_DTYPE;
-    const int64_t elems = checked_count(batch, L, dim);
-    const int64_t bcn = checked_count(batch, L, N > 0 ? N : 1);
-    const int64_t states = checked_count(batch, dim, N > 0 ? N : 1);
-    if (elems < 0 || bcn < 0 || states < 0 || N < 1)
-        return SELSCAN_ERR_SHAPE;
-    if (!u || !delta || !A || !Bm || !Cm || !dy || !du || !ddelta || !dA || !dB || !dC ||
-        (z && !dz))
-        return SELSCAN_ERR_NULL;
-    if (!supported_n(N) || dim > kMaxDim)
+    return bwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, dy, dh_last,
+                      du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr, nullptr,
+                      nullptr, batch, L, dim, N, dtype, workspace, workspace_bytes, stream);
+}
+
+int selscan_bwd_ex(const void *u, const void *delta, const float *A, const void *Bm,
+                   const void *Cm, const float *D_skip, const void *z, const float *delta_bias,
+                   int delta_softplus, const float *h0, const void *dy, const float *dh_last,
+                   void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz,
+                   float *ddelta_bias, float *dh0, int flags, const float *conv_weight,
+                   const float *conv_bias, int64_t conv_width, float *dconv_weight,
+                   float *dconv_bias, int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE))
         return SELSCAN_ERR_UNSUPPORTED;
-    if (!z)
-        dz = nullptr;
-    const void *all[] = {u,  delta, A,  Bm, Cm, D_skip, z,  delta_bias,  h0,  dy,       dh_last,
-                         du, ddelta, dA, dB, dC, dD,     dz, ddelta_bias, dh0, workspace};
-    for (const void *p : all)
-        if (p && !aligned16(p))
-            return SELSCAN_ERR_UNSUPPORTED;
-    const size_t need = selscan_bwd_workspace_bytes(batch, L, dim, N, dtype);
-    if (!workspace || workspace_bytes < need)
-        return SELSCAN_ERR_WORKSPACE;
-
-    const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
-    const Range ins[] = {{u, elems * es},       {delta, elems * es},   {A, dim * N * 4},
-                         {Bm, bcn * es},        {Cm, bcn * es},        {D_skip, dim * 4},
-                         {z, elems * es},       {delta_bias, dim * 4}, {h0, states * 4},
-                         {dy, elems * es},      {dh_last, states * 4}, {workspace, (int64_t)need}};
-    const Range outs[] = {{du, elems * es}, {ddelta, elems * es}, {dA, dim * N * 4},
-                          {dB, bcn * 4},    {dC, bcn * 4},        {dD, dim * 4},
-                          {dz, elems * es}, {ddelta_bias, dim * 4}, {dh0, states * 4}};
-    for (const Range &o : outs)
-        for (const Range &i : ins)
-            if (overlaps(o, i))
-                return SELSCAN_ERR_ALIAS;
-    const int n_out = (int)(sizeof(outs) / sizeof(outs[0]));
-    for (int i = 0; i < n_out; ++i)
-        for (int j = i + 1; j < n_out; ++j)
-            if (overlaps(outs[i], outs[j]))
-                return SELSCAN_ERR_ALIAS;
-
-    selscan::BwdArgs a;
-    selscan::FwdArgs &f = a.fwd;
-    f.u = u; f.delta = delta; f.A = A; f.Bm = Bm; f.Cm = Cm; f.D_skip = D_skip; f.z = z;
-    f.delta_bias = delta_bias; f.delta_softplus = delta_softplus ? 1 : 0; f.h0 = h0;
-    f.y = nullptr; f.h_last = nullptr; f.batch = batch; f.L = L; f.dim = dim; f.N = N;
-    f.dtype = dtype; f.workspace = workspace; f.workspace_bytes = workspace_bytes;
-    a.dy = dy; a.dh_last = dh_last; a.du = du; a.ddelta = ddelta; a.dz = dz; a.dA = dA;
-    a.dB = dB; a.dC = dC; a.dD = dD; a.ddelta_bias = ddelta_bias; a.dh0 = dh0;
-    return finish_launch(selscan::launch_bwd(a, (hipStream_t)stream));
+    if (conv_width < 0)
+        return SELSCAN_ERR_SHAPE;
+    if (conv_width > SELSCAN_MAX_CONV_WIDTH)
+        return SELSCAN_ERR_UNSUPPORTED;
+    selscan::FwdExt e;
+    e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |
+              (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0);
+    e.conv_w = conv_weight;
+    e.conv_b = conv_bias;
+    e.conv_k = (int)conv_width;
+    return bwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, dy, dh_last,
+                      du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, &e, dconv_weight,
+                      dconv_bias, batch, L, dim, N, dtype, workspace, workspace_bytes, stream);
 }
 
 int selscan_state_update(float *state, const void *u, const void *delta, const float *A,

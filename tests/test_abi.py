@@ -43,7 +43,7 @@ def header_constant(name):
 def test_library_exports_every_declared_symbol():
     L = ss.lib()
     names = header_functions()
-    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_bwd", "selscan_state_update",
+    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_bwd", "selscan_bwd_ex", "selscan_state_update",
             "selscan_fwd_workspace_bytes", "selscan_bwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), "missing export " + n
@@ -222,6 +222,47 @@ INVALID_BWD = [
 def test_bwd_rejects_invalid_arguments(name, kw, status):
     L = ss.lib()
     assert L.selscan_bwd(*bwd_args(**kw)) == status
+    assert L.selscan_last_hip_error() == 0
+
+
+def bwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, dconv_w=None, dconv_b=None,
+                **kw):
+    a = bwd_args(**kw)
+    # flags, conv_weight, conv_bias, conv_width, dconv_weight, dconv_bias go
+    # between dh0 and batch
+    return a[:21] + [flags, conv_w, conv_b, conv_width, dconv_w, dconv_b] + a[21:]
+
+
+INVALID_BWD_EX = [
+    ("unknown_flag", dict(flags=8), ERR_UNSUP),
+    ("conv_width_5", dict(conv_width=5, conv_w=fake(22), dconv_w=fake(24)), ERR_UNSUP),
+    ("conv_width_neg", dict(conv_width=-2, conv_w=fake(22), dconv_w=fake(24)), ERR_SHAPE),
+    ("conv_w_null", dict(conv_width=4, dconv_w=fake(24)), ERR_NULL),
+    ("dconv_w_null", dict(conv_width=4, conv_w=fake(22)), ERR_NULL),
+    ("dconv_b_misaligned", dict(conv_width=3, conv_w=fake(22), dconv_w=fake(24),
+                                dconv_b=ctypes.c_void_p(BASE + 25 * STEP + 4)), ERR_UNSUP),
+    ("dconv_w_aliases_conv_w", dict(conv_width=4, conv_w=fake(22),
+                                    dconv_w=ctypes.c_void_p(BASE + 22 * STEP + 64)), ERR_ALIAS),
+    ("dconv_b_aliases_du", dict(conv_width=4, conv_w=fake(22), dconv_w=fake(24),
+                                dconv_b=ctypes.c_void_p(BASE + 12 * STEP + 256)), ERR_ALIAS),
+    ("dconv_w_aliases_dconv_b", dict(conv_width=4, conv_w=fake(22), dconv_w=fake(24),
+                                     dconv_b=ctypes.c_void_p(BASE + 24 * STEP + 128)), ERR_ALIAS),
+    ("du_aliases_conv_b", dict(conv_width=2, conv_w=fake(22), conv_b=fake(23), dconv_w=fake(24),
+                               du=ctypes.c_void_p(BASE + 23 * STEP)), ERR_ALIAS),
+    # the checks of selscan_bwd apply as well
+    ("dtype", dict(dtype=4, flags=1), ERR_DTYPE),
+    ("N3", dict(N=3, flags=2), ERR_UNSUP),
+    ("dy_null", dict(dy=None, flags=3), ERR_NULL),
+    ("small_workspace", dict(workspace_bytes=4096, conv_width=4, conv_w=fake(22),
+                             dconv_w=fake(24)), ERR_WS),
+]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("name,kw,status", INVALID_BWD_EX, ids=[c[0] for c in INVALID_BWD_EX])
+def test_bwd_ex_rejects_invalid_arguments(name, kw, status):
+    L = ss.lib()
+    assert L.selscan_bwd_ex(*bwd_ex_args(**kw)) == status
     assert L.selscan_last_hip_error() == 0
 
 

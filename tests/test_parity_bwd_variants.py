@@ -1,0 +1,221 @@
+"""GPU parity of the variant backward (selscan_bwd_ex) against the fp64 oracle.
+
+The variants are those of selscan_fwd_ex: the exact zero-order-hold B_bar, the
+reverse scan direction and the fused causal conv1d + SiLU prologue, alone and
+combined.  Every gradient, the conv taps' and bias' included, is compared
+element by element with ``oracle.bwd`` (same flags and conv) on the same
+seeded inputs and upstream gradients, with the metric and tolerances of the
+other parity tests.  The reverse direction is also checked bit for bit
+against the forward-direction backward on the flipped sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selscan_inputs as si
+import selective_state_space_selscan_amd as ss
+from parity_util import TOL, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+ZOH, REV = ss.SELSCAN_FLAG_ZOH_EXACT, ss.SELSCAN_FLAG_REVERSE
+NAMES = ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0", "dconv_weight",
+         "dconv_bias")
+ORACLE_NAME = {"ddelta_bias": "dbias", "dconv_weight": "dconv_w", "dconv_bias": "dconv_b"}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def upstream(inp, seed, with_dh_last=True):
+    rng = np.random.default_rng([seed, 4343])
+    dy = rng.standard_normal((inp.batch, inp.L, inp.dim)).astype(np.float32)
+    if inp.dtype == si.BF16:
+        dy = si.bf16_round_np(dy)[1]
+    dhl = rng.standard_normal((inp.batch, inp.dim, inp.N)).astype(np.float32) \
+        if with_dh_last else None
+    return dy, dhl
+
+
+def run_bwd_ex(inp, dy, dhl, device, flags, conv, softplus=True, flip=False):
+    t = si.fwd_tensors(inp, device)
+    f = (lambda x: x.flip(1).contiguous()) if flip else (lambda x: x)
+    tdy = f(torch.from_numpy(dy).to(device).to(t["u"].dtype))
+    tdhl = None if dhl is None else torch.from_numpy(dhl).to(device)
+    cw = cb = None
+    if conv is not None:
+        cw = torch.from_numpy(conv[0]).to(device)
+        cb = None if conv[1] is None else torch.from_numpy(conv[1]).to(device)
+    z = None if t["z"] is None else f(t["z"])
+    g = ss.selscan_bwd_ex(f(t["u"]), f(t["delta"]), t["A"], f(t["Bm"]), f(t["Cm"]), tdy,
+                          t["D_skip"], z, t["delta_bias"], softplus, t["h0"], tdhl, flags=flags,
+                          conv_weight=cw, conv_bias=cb)
+    torch.cuda.synchronize()
+    return g
+
+
+def check_bwd_ex(inp, device, seed, flags, conv=None, what="", softplus=True, with_dh_last=True,
+                 tol=None):
+    tol = TOL[inp.dtype] if tol is None else tol
+    say("case", what, "flags", flags, "conv", None if conv is None else conv[0].shape,
+        inp.batch, inp.L, inp.dim, inp.N, inp.dtype)
+    dy, dhl = upstream(inp, seed, with_dh_last)
+    g = run_bwd_ex(inp, dy, dhl, device, flags, conv, softplus)
+    w, b = (None, None) if conv is None else conv
+    ref = oracle.bwd(inp.u.value, inp.delta.value, inp.A, inp.Bm.value, inp.Cm.value, dy,
+                     inp.D_skip, None if inp.z is None else inp.z.value, inp.delta_bias,
+                     softplus, inp.h0, dhl, flags=flags, conv_w=w, conv_b=b)
+    errs = {}
+    for k in NAMES:
+        r = ref[ORACLE_NAME.get(k, k)]
+        if g.get(k) is None or r is None:
+            assert g.get(k) is None and r is None, k
+            continue
+        errs[k] = rel_err(to_np(g[k]), r)
+    say("  rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()) + " (tol %.1g)" % tol)
+    bad = {k: e for k, e in errs.items() if not e <= tol}
+    assert not bad, bad
+    return g
+
+
+CONVS = {"none": None, "k4_bias": (4, True), "k2": (2, False), "k1_bias": (1, True)}
+
+
+def conv_for(name, dim, seed):
+    c = CONVS[name]
+    return None if c is None else si.conv_params(dim, c[0], seed, c[1])
+
+
+VARIANTS = [(f, c) for f in (0, ZOH, REV, ZOH | REV) for c in ("none", "k4_bias", "k2")
+            if (f, c) != (0, "none")]
+
+
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+@pytest.mark.parametrize("flags,conv", VARIANTS, ids=["f%d-%s" % v for v in VARIANTS])
+def test_bwd_variants_medium(device, flags, conv, dtype):
+    """Several channel groups, lanes past dim, a ragged tail and many parts
+    (the summaries, the fold and the conv fix-up at part boundaries run)."""
+    inp = si.make_fwd_inputs(2, 777, 130, 16, dtype, True, seed=1400 + flags, h0=True)
+    check_bwd_ex(inp, device, 1401 + flags, flags, conv_for(conv, 130, 1402 + flags),
+                 what="medium/" + conv)
+
+
+@pytest.mark.parametrize("N", [4, 8, 32, 64])
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+def test_bwd_variants_every_state_size(device, N, dtype):
+    inp = si.make_fwd_inputs(2, 300, 96, N, dtype, True, seed=1420 + N, h0=True)
+    check_bwd_ex(inp, device, 1421 + N, ZOH | REV, si.conv_params(96, 4, 1422 + N),
+                 what="N%d" % N)
+    check_bwd_ex(inp, device, 1423 + N, ZOH, None, what="N%d zoh" % N)
+    check_bwd_ex(inp, device, 1424 + N, REV, conv_for("k1_bias", 96, 1425 + N),
+                 what="N%d rev conv1" % N)
+
+
+@pytest.mark.parametrize("flags", [ZOH, REV, ZOH | REV])
+@pytest.mark.parametrize("N,L", [(16, 900), (4, 300), (64, 250)])
+def test_bwd_variants_unstructured_A(device, flags, N, L):
+    """A that is not (n+1) A[d,0], spread over decades: the exp2 path and,
+    with exact ZOH, both branches of the coefficient and of its derivative."""
+    inp = si.make_fwd_inputs(2, L, 160, N, si.F32, True, seed=1440 + N, h0=True)
+    rng = np.random.default_rng(1441 + N)
+    inp.A = (-np.exp(rng.uniform(-4.0, 2.5, size=(160, N)))).astype(np.float32)
+    check_bwd_ex(inp, device, 1442 + N, flags, si.conv_params(160, 3, 1443), what="unstructured")
+
+
+def test_bwd_zoh_small_and_zero_A(device):
+    """|Delta A| tiny (series branches everywhere) and A = 0 exactly
+    (B_bar = Delta B, dc/dA = Delta^2 / 2), structured and not."""
+    inp = si.make_fwd_inputs(1, 400, 128, 16, si.F32, True, seed=1460, h0=True)
+    for name, A in [("tiny_structured", si.s4d_real_A(128, 16) * 1e-6),
+                    ("zero", np.zeros((128, 16), np.float32)),
+                    ("mixed_zero", np.where(np.arange(16) % 3 == 0, 0.0,
+                                            si.s4d_real_A(128, 16)).astype(np.float32))]:
+        inp.A = np.ascontiguousarray(A, dtype=np.float32)
+        check_bwd_ex(inp, device, 1461, ZOH, None, what="zoh/" + name)
+        check_bwd_ex(inp, device, 1462, ZOH | REV, si.conv_params(128, 4, 1463),
+                     what="zoh_rev_conv/" + name)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64), (1, 2, 1), (3, 3, 100), (2, 5, 65),
+                                   (1, 17, 130), (1, 20, 64), (2, 2049, 64)])
+def test_bwd_variants_ragged(device, shape):
+    """Sequences shorter than the conv window, single steps, lanes past dim,
+    a last part of one step (2049), parts of four steps (20)."""
+    batch, L, dim = shape
+    inp = si.make_fwd_inputs(batch, L, dim, 16, si.BF16, True, seed=1480 + sum(shape), h0=True)
+    check_bwd_ex(inp, device, 1481 + sum(shape), ZOH | REV, si.conv_params(dim, 4, 1482),
+                 what="ragged")
+    check_bwd_ex(inp, device, 1483 + sum(shape), 0, si.conv_params(dim, 3, 1484, False),
+                 what="ragged")
+
+
+def test_bwd_variants_minimal_arguments(device):
+    """No gate, D, bias, h0, dh_last or conv bias."""
+    inp = si.make_fwd_inputs(2, 500, 64, 16, si.F32, False, seed=1500, h0=False,
+                             with_bias=False, D_value=None)
+    inp.D_skip = None
+    check_bwd_ex(inp, device, 1501, ZOH | REV, si.conv_params(64, 4, 1502, False),
+                 what="minimal", with_dh_last=False)
+
+
+def test_bwd_variants_without_softplus(device):
+    inp = si.make_fwd_inputs(2, 600, 96, 16, si.F32, True, seed=1510, h0=True)
+    inp.delta.value[:] = np.abs(inp.delta.value) * 0.05
+    inp.delta_bias = np.full(96, 1e-3, np.float32)
+    check_bwd_ex(inp, device, 1511, ZOH | REV, si.conv_params(96, 4, 1512), softplus=False,
+                 what="no_softplus")
+
+
+def test_bwd_ex_without_variants_matches_bwd(device):
+    """flags = 0 without conv through selscan_bwd_ex is selscan_bwd, bit for bit."""
+    inp = si.make_fwd_inputs(2, 1000, 200, 16, si.BF16, True, seed=1520, h0=True)
+    dy, dhl = upstream(inp, 1521)
+    g0 = run_bwd_ex(inp, dy, dhl, device, 0, None)
+    t = si.fwd_tensors(inp, device)
+    g1 = ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"],
+                        torch.from_numpy(dy).to(device).to(t["u"].dtype), t["D_skip"], t["z"],
+                        t["delta_bias"], True, t["h0"], torch.from_numpy(dhl).to(device))
+    torch.cuda.synchronize()
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g0[k], g1[k]), k
+
+
+@pytest.mark.parametrize("flags,conv", [(ZOH | REV, "k4_bias"), (REV, "none")])
+def test_bwd_reverse_is_forward_on_flipped_sequence_bitwise(device, flags, conv):
+    """REVERSE runs the same scan-order arithmetic over flipped addresses, so
+    its gradients are those of the forward direction on the flipped inputs,
+    bit for bit (per-timestep ones flipped back)."""
+    inp = si.make_fwd_inputs(2, 1234, 192, 16, si.BF16, True, seed=1530, h0=True)
+    dy, dhl = upstream(inp, 1531)
+    c = conv_for(conv, 192, 1532)
+    g_r = run_bwd_ex(inp, dy, dhl, device, flags, c)
+    g_f = run_bwd_ex(inp, dy, dhl, device, flags & ~REV, c, flip=True)
+    for k in NAMES:
+        if g_r.get(k) is None:
+            continue
+        other = g_f[k].flip(1) if k in ("du", "ddelta", "dz", "dB", "dC") else g_f[k]
+        assert torch.equal(g_r[k], other), k
+
+
+def test_bwd_variants_bitwise_repeatable(device):
+    inp = si.make_fwd_inputs(2, 1500, 200, 16, si.BF16, True, seed=1540, h0=True)
+    dy, dhl = upstream(inp, 1541)
+    c = si.conv_params(200, 4, 1542)
+    g1 = run_bwd_ex(inp, dy, dhl, device, ZOH | REV, c)
+    g2 = run_bwd_ex(inp, dy, dhl, device, ZOH | REV, c)
+    for k in NAMES:
+        if g1.get(k) is not None:
+            assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("flags", [REV, ZOH | REV])
+def test_bwd_variants_layer_workload(device, flags):
+    """The 130M-layer shape (batch 8, L 2048, D 1536, N 16, bf16, gate, D,
+    bias) with the conv prologue (k = 4, bias), every gradient in full."""
+    w = si.WORKLOADS["mamba130m_layer"]
+    inp = si.workload_fwd_inputs(w)
+    check_bwd_ex(inp, device, 1550 + flags, flags, si.conv_params(w.dim, 4, 1551),
+                 what="mamba130m_layer", with_dh_last=False)
