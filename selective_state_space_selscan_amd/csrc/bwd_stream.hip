@@ -61,8 +61,11 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N)
                         kLanes * 4;
     const size_t slots = (size_t)batch * w.p.parts;
     size_t off = 0;
+    const size_t entry = (size_t)w.p.groups * w.p.parts * N * kLanes * 4;
     w.fsumm = off; off = align256(off + summ);
     w.asumm = off; off = align256(off + summ);
+    w.fentry = off; off = align256(off + entry);
+    w.aentry = off; off = align256(off + entry);
     w.ckpt = off; off = align256(off + (size_t)w.p.groups * w.nck * N * kLanes * 4);
     w.pB = off; off = align256(off + (size_t)w.gpr * batch * L * N * 4);
     w.pC = off; off = align256(off + (size_t)w.gpr * batch * L * N * 4);

@@ -19,8 +19,10 @@
 //   2. adjoint part summaries, for the fold from the right: over a part
 //      [s, e), the adjoint leaving it to the left is
 //        g_{s-1} = sum_t (prod_{k=s..t} A_bar_k) C_t dypre_t
-//                  + exp(A sum_part Delta) g_{e-1},
-//      the same associative operator as the forward, in reverse;
+//        + exp(A sum_part Delta) g_{e-1},
+//      the same associative operator as the forward, in reverse; the carry
+//      kernel of the forward then folds h0 from the left and dh_last from
+//      the right into the entry state of every part, both directions;
 //   3. checkpoints: each part walked forward from its entry state, storing
 //      the state at the start of every TT-step chunk (fp32, in the workspace);
 //   4. the main pass: each part walked backwards chunk by chunk; a chunk's
@@ -329,7 +331,7 @@ template <int N, int VAR, typename TIO>
 __global__ __launch_bounds__(kLanes * 4) void bwd_checkpoint_kernel(
     const TIO *__restrict__ u, const TIO *__restrict__ delta, const float *__restrict__ A,
     const TIO *__restrict__ Bm, const float *__restrict__ delta_bias, int delta_softplus,
-    const float *__restrict__ h0, const float *__restrict__ fsumm, float *__restrict__ ckpt,
+    const float *__restrict__ h0, const float *__restrict__ fentry, float *__restrict__ ckpt,
     int64_t L, int64_t dim, int64_t groups, int parts, int64_t part_len, int64_t nck,
     ExtParams ext)
 {
@@ -353,12 +355,16 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_checkpoint_kernel(
         stream::conv_taps(c, ext, w.d);
         stream::conv_window<VAR>(win, c, u, w.d);
     }
+    // entry state: h0 carried through the earlier parts (fentry, null when
+    // the sequence is not split)
     float h[N];
+    if (fentry) {
+        stream::load_entry<N>(h, fentry, w.grp, parts, w.part, w.lane);
+    } else {
 #pragma unroll
-    for (int n = 0; n < N; ++n)
-        h[n] = h0 ? h0[(c.b * dim + w.d) * N + n] : 0.0f;
-    stream::fold_summaries<N>(h, fsumm + (w.grp * (parts - 1)) * (N + 1) * kLanes + w.lane, 0,
-                              w.part, 1, pow_path, A2, c.A2_0);
+        for (int n = 0; n < N; ++n)
+            h[n] = h0 ? h0[(c.b * dim + w.d) * N + n] : 0.0f;
+    }
     float *ck = ckpt + w.grp * nck * (N * kLanes) + w.lane;
     // with kVarExt the softplus switch is read at run time (SP unused)
     const bool sp = (VAR & kVarExt) != 0 || delta_softplus;
@@ -679,7 +685,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     const TIO *__restrict__ dy, const float *__restrict__ A, const TIO *__restrict__ Bm,
     const TIO *__restrict__ Cm, const float *__restrict__ D_skip,
     const float *__restrict__ delta_bias, int delta_softplus, const float *__restrict__ dh_last,
-    const float *__restrict__ asumm, const float *__restrict__ ckpt, BwdOut o, int64_t L,
+    const float *__restrict__ aentry, const float *__restrict__ ckpt, BwdOut o, int64_t L,
     int64_t dim, int64_t batch, int64_t groups, int parts, int64_t part_len, int64_t nck,
     ExtParams ext)
 {
@@ -698,14 +704,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     if constexpr (CONV)
         stream::conv_taps(c, ext, w.d);
     // adjoint entering the part's last step from the right: dh_last folded
-    // through the summaries of the later parts
+    // through the adjoint summaries of the later parts (aentry, null when the
+    // sequence is not split)
     float g[N];
+    if (aentry) {
+        stream::load_entry<N>(g, aentry, w.grp, parts, w.part, w.lane);
+    } else {
 #pragma unroll
-    for (int n = 0; n < N; ++n)
-        g[n] = dh_last ? dh_last[(c.b * dim + w.d) * N + n] : 0.0f;
-    // adjoint summary of part q is entry q - 1; fold parts P-1 down to part+1
-    stream::fold_summaries<N>(g, asumm + (w.grp * (parts - 1)) * (N + 1) * kLanes + w.lane,
-                              parts - 2, parts - 1 - w.part, -1, pow_path, A2, c.A2_0);
+        for (int n = 0; n < N; ++n)
+            g[n] = dh_last ? dh_last[(c.b * dim + w.d) * N + n] : 0.0f;
+    }
     float dA[N];
 #pragma unroll
     for (int n = 0; n < N; ++n)
@@ -793,7 +801,8 @@ hipError_t launch_colsum(const float *in, float *out, int64_t P, int64_t K, hipS
 struct BwdLayout {
     StreamPlan p;
     int64_t nck, gpr;
-    size_t fsumm, asumm, ckpt, pB, pC, pA, pD, pbias, pW, pWb, xown, xcarry, total;   // bytes
+    size_t fsumm, asumm, fentry, aentry, ckpt, pB, pC, pA, pD, pbias, pW, pWb, xown, xcarry,
+        total;   // byte offsets
 };
 BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N);
 
@@ -804,6 +813,7 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     const BwdLayout w = bwd_layout(a.fwd.batch, a.fwd.L, a.fwd.dim, N);
     char *base = (char *)(((uintptr_t)a.fwd.workspace + 255) & ~(uintptr_t)255);
     float *fsumm = (float *)(base + w.fsumm), *asumm = (float *)(base + w.asumm);
+    float *fentry = (float *)(base + w.fentry), *aentry = (float *)(base + w.aentry);
     float *ckpt = (float *)(base + w.ckpt);
     BwdOut o;
     o.du = a.du; o.ddelta = a.ddelta; o.dz = a.dz;
@@ -835,21 +845,28 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
                            asumm, a.fwd.L, a.fwd.dim, p.groups, p.parts, p.part_len, x.rev);
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
+        // entry states of the parts: h0 from the left, dh_last from the right
+        if ((err = launch_fwd_carry(fsumm, a.fwd.h0, a.fwd.A, fentry, a.fwd.batch, a.fwd.dim, N,
+                                    p.parts, 0, s)) != hipSuccess ||
+            (err = launch_fwd_carry(asumm, a.dh_last, a.fwd.A, aentry, a.fwd.batch, a.fwd.dim, N,
+                                    p.parts, 1, s)) != hipSuccess)
+            return err;
     }
+    const bool split = p.parts > 1;
     const int64_t waves = p.groups * p.parts;
     hipLaunchKernelGGL((bwd_checkpoint_kernel<N, VAR, TIO>), dim3((unsigned)((waves + 3) / 4)),
                        dim3(kLanes * 4), 0, s, (const TIO *)a.fwd.u, (const TIO *)a.fwd.delta,
                        a.fwd.A, (const TIO *)a.fwd.Bm, a.fwd.delta_bias, a.fwd.delta_softplus,
-                       a.fwd.h0, fsumm, ckpt, a.fwd.L, a.fwd.dim, p.groups, p.parts, p.part_len,
-                       w.nck, x);
+                       a.fwd.h0, (const float *)(split ? fentry : nullptr), ckpt, a.fwd.L,
+                       a.fwd.dim, p.groups, p.parts, p.part_len, w.nck, x);
     if ((err = hipGetLastError()) != hipSuccess)
         return err;
     hipLaunchKernelGGL((bwd_main_kernel<N, VAR, TIO>), dim3((unsigned)waves), dim3(kLanes), 0, s,
                        (const TIO *)a.fwd.u, (const TIO *)a.fwd.delta, (const TIO *)a.fwd.z,
                        (const TIO *)a.dy, a.fwd.A, (const TIO *)a.fwd.Bm, (const TIO *)a.fwd.Cm,
-                       a.fwd.D_skip, a.fwd.delta_bias, a.fwd.delta_softplus, a.dh_last, asumm,
-                       ckpt, o, a.fwd.L, a.fwd.dim, a.fwd.batch, p.groups, p.parts, p.part_len,
-                       w.nck, x);
+                       a.fwd.D_skip, a.fwd.delta_bias, a.fwd.delta_softplus, a.dh_last,
+                       (const float *)(split ? aentry : nullptr), ckpt, o, a.fwd.L, a.fwd.dim,
+                       a.fwd.batch, p.groups, p.parts, p.part_len, w.nck, x);
     if ((err = hipGetLastError()) != hipSuccess)
         return err;
     if (CONV && p.parts > 1) {

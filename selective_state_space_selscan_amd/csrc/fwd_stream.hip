@@ -9,18 +9,23 @@
 namespace selscan {
 
 // SELSCAN_STREAM_PARTS=P overrides the number of sequence parts (tuning knob).
-// Default (measured on MI355X): about one wave per wave slot of the chip (1024
-// SIMDs x the kernel's waves per SIMD) when the channel groups are few; with
-// many groups, at least 8 parts (when L allows), since smaller waves balance
-// the tail of the grid better than fewer, longer ones.  Parts are whole
-// multiples of kStreamTT steps and at least 4 of them long.
-StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd)
+// Default (measured on MI355X): waves_per_slot_x2 / 2 waves per wave slot of
+// the chip (1024 SIMDs x the kernel's waves per SIMD) when the channel groups
+// are few; with many groups, at least 8 parts (when L allows), since smaller
+// waves balance the tail of the grid better than fewer, longer ones.  Where
+// each main-pass wave folds the summaries of the parts before it, the fold
+// grows with the part count, so those plans aim at one wave per slot; with
+// carried entry states, 1.5 (mamba130m_layer: 32 parts of 64 steps, 8% faster
+// than 22 parts; long_seq 192 parts).  Parts are whole multiples of kStreamTT
+// steps and at least 4 of them long.
+StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd,
+                            int waves_per_slot_x2)
 {
     constexpr int kLanes = stream::kLanes;
     constexpr int TT = kStreamTT;
     StreamPlan p;
     p.groups = batch * ((dim + kLanes - 1) / kLanes);
-    const int64_t target_waves = 1024 * (int64_t)waves_per_simd;
+    const int64_t target_waves = 512 * (int64_t)waves_per_simd * waves_per_slot_x2;
     int64_t parts = (target_waves + p.groups - 1) / p.groups;
     const int64_t min_parts = L / 256 < 8 ? L / 256 : 8;
     if (parts < min_parts)
@@ -44,23 +49,118 @@ StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per
 
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N)
 {
-    // the default plan has the most parts (the variants' plans aim at fewer waves)
-    const StreamPlan p = make_stream_plan(batch, L, dim, 4);
-    return p.parts > 1 ? (size_t)p.groups * (p.parts - 1) * (N + 1) * stream::kLanes * 4 + 256 : 0;
+    // the default forward's plan has the most parts (the other plans aim at
+    // fewer waves): the part summaries, then the entry states of the parts
+    const StreamPlan p = make_stream_plan(batch, L, dim, 4, kDefaultFwdSlotsX2);
+    if (p.parts <= 1)
+        return 0;
+    const size_t summ = (size_t)p.groups * (p.parts - 1) * (N + 1) * stream::kLanes * 4;
+    const size_t entry = (size_t)p.groups * p.parts * N * stream::kLanes * 4;
+    return 256 + ((summ + 255) & ~(size_t)255) + entry;
+}
+
+namespace {
+
+// Entry states of the parts from the part summaries: the exclusive prefix of
+// the associative fold h <- exp(A S) h + x (S the part's sum of Delta, x its
+// end state from zero).  One lane per (channel group, state n, channel): the
+// fold runs over the parts in sequence, its loads kCarryBatch parts ahead.
+//   forward (reverse = 0): entry[0] = init (h0, or 0), and entry[j + 1] =
+//     summary j folded into entry[j];
+//   reverse (reverse = 1, the backward's adjoint): entry[P-1] = init
+//     (dh_last, or 0), and entry[j] = summary j (that of part j + 1) folded
+//     into entry[j + 1].
+// summ: (groups, P - 1, N + 1, 64); entry: (groups, P, N, 64); init:
+// (batch, dim, N) or null.
+constexpr int kCarryBatch = 16;
+
+template <int N>
+__global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ summ,
+                                                    const float *__restrict__ init,
+                                                    const float *__restrict__ A,
+                                                    float *__restrict__ entry, int64_t dim,
+                                                    int64_t groups, int parts, int reverse)
+{
+    constexpr int kLanes = stream::kLanes;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = (int)(tid & (kLanes - 1));
+    const int64_t wn = tid / kLanes;   // (group, n), wave-uniform
+    if (wn >= groups * N)
+        return;
+    const int n = (int)(wn % N);
+    const int64_t grp = wn / N;
+    const int64_t gpr = (dim + kLanes - 1) / kLanes;
+    const int64_t b = grp / gpr;
+    const int64_t d0 = (grp % gpr) * kLanes;
+    const int64_t d = d0 + lane < dim ? d0 + lane : dim - 1;
+    const float a2 = A[d * N + n] * kLog2e;
+    float h = init ? init[(b * dim + d) * N + n] : 0.0f;
+    const int64_t sstride = (int64_t)(N + 1) * kLanes;   // between summaries
+    const int64_t estride = (int64_t)N * kLanes;         // between entry states
+    const float *sb = summ + grp * (parts - 1) * sstride + lane;
+    float *eb = entry + grp * parts * estride + n * kLanes + lane;
+    const int J = parts - 1;
+    eb[(reverse ? J : 0) * estride] = h;
+    for (int k0 = 0; k0 < J; k0 += kCarryBatch) {
+        float S[kCarryBatch], X[kCarryBatch];
+#pragma unroll
+        for (int k = 0; k < kCarryBatch; ++k) {
+            const int j = reverse ? J - 1 - (k0 + k) : k0 + k;
+            const bool in = k0 + k < J;
+            S[k] = in ? sb[j * sstride] : 0.0f;
+            X[k] = in ? sb[j * sstride + (n + 1) * kLanes] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kCarryBatch; ++k) {
+            if (k0 + k < J) {
+                const int j = reverse ? J - 1 - (k0 + k) : k0 + k;
+                h = fmaf(hw_exp2(a2 * S[k]), h, X[k]);
+                eb[(reverse ? j : j + 1) * estride] = h;
+            }
+        }
+    }
+}
+
+template <int N>
+hipError_t carry_n(const float *summ, const float *init, const float *A, float *entry,
+                   int64_t batch, int64_t dim, int parts, int reverse, hipStream_t s)
+{
+    const int64_t groups = batch * ((dim + stream::kLanes - 1) / stream::kLanes);
+    const int64_t threads = groups * N * stream::kLanes;
+    hipLaunchKernelGGL((carry_kernel<N>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       s, summ, init, A, entry, dim, groups, parts, reverse);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_fwd_carry(const float *summ, const float *init, const float *A, float *entry,
+                            int64_t batch, int64_t dim, int64_t N, int parts, int reverse,
+                            hipStream_t stream)
+{
+    switch (N) {
+    case 4: return carry_n<4>(summ, init, A, entry, batch, dim, parts, reverse, stream);
+    case 8: return carry_n<8>(summ, init, A, entry, batch, dim, parts, reverse, stream);
+    case 16: return carry_n<16>(summ, init, A, entry, batch, dim, parts, reverse, stream);
+    case 32: return carry_n<32>(summ, init, A, entry, batch, dim, parts, reverse, stream);
+    case 64: return carry_n<64>(summ, init, A, entry, batch, dim, parts, reverse, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 namespace {
 
 template <typename TIO>
-hipError_t launch_default(const FwdArgs &a, const StreamPlan &p, float *summ, hipStream_t s)
+hipError_t launch_default(const FwdArgs &a, const StreamPlan &p, float *summ, float *entry,
+                          hipStream_t s)
 {
     const stream::ExtParams none = {nullptr, nullptr, 0, 0};
     switch (a.N) {
-    case 4: return stream::launch_n<4, 0, TIO>(a, none, p, summ, s);
-    case 8: return stream::launch_n<8, 0, TIO>(a, none, p, summ, s);
-    case 16: return stream::launch_n<16, 0, TIO>(a, none, p, summ, s);
-    case 32: return stream::launch_n<32, 0, TIO>(a, none, p, summ, s);
-    case 64: return stream::launch_n<64, 0, TIO>(a, none, p, summ, s);
+    case 4: return stream::launch_n<4, 0, TIO>(a, none, p, summ, entry, s);
+    case 8: return stream::launch_n<8, 0, TIO>(a, none, p, summ, entry, s);
+    case 16: return stream::launch_n<16, 0, TIO>(a, none, p, summ, entry, s);
+    case 32: return stream::launch_n<32, 0, TIO>(a, none, p, summ, entry, s);
+    case 64: return stream::launch_n<64, 0, TIO>(a, none, p, summ, entry, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -69,10 +169,11 @@ hipError_t launch_default(const FwdArgs &a, const StreamPlan &p, float *summ, hi
 
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream)
 {
-    const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim);
+    const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, 4, kDefaultFwdSlotsX2);
     float *summ = stream::summary_buffer(a.workspace);
-    return a.dtype == 1 ? launch_default<uint16_t>(a, p, summ, stream)
-                        : launch_default<float>(a, p, summ, stream);
+    float *entry = stream::entry_buffer(a.workspace, p, a.N);
+    return a.dtype == 1 ? launch_default<uint16_t>(a, p, summ, entry, stream)
+                        : launch_default<float>(a, p, summ, entry, stream);
 }
 
 namespace {
@@ -91,7 +192,8 @@ hipError_t summaries_n(const FwdArgs &a, const StreamPlan &p, float *summ, hipSt
                        (const TIO *)a.delta, (const TIO *)nullptr, (TIO *)nullptr, a.A,
                        (const TIO *)a.Bm, (const TIO *)a.Cm, (const float *)nullptr,
                        a.delta_bias, a.delta_softplus, (const float *)nullptr, (float *)nullptr,
-                       summ, a.L, a.dim, p.groups, p.parts, p.part_len, none);
+                       summ, (const float *)nullptr, a.L, a.dim, p.groups, p.parts, p.part_len,
+                       none);
     return hipGetLastError();
 }
 

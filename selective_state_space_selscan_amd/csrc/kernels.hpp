@@ -58,8 +58,12 @@ struct StreamPlan {
     int64_t part_len;   // steps per sequence part
     int parts;
 };
-// waves_per_simd: the kernel's occupancy (the plan aims at one wave per slot).
-StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd = 4);
+// waves_per_simd: the kernel's occupancy; the plan aims at waves_per_slot_x2 / 2
+// waves per wave slot of the chip (3: the default forward, whose main pass
+// reads carried entry states; 2: plans whose main pass folds the summaries).
+StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd = 4,
+                            int waves_per_slot_x2 = 2);
+constexpr int kDefaultFwdSlotsX2 = 3;
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
 
@@ -91,6 +95,14 @@ SELSCAN_DECLARE_EXT(16)
 SELSCAN_DECLARE_EXT(32)
 SELSCAN_DECLARE_EXT(64)
 #undef SELSCAN_DECLARE_EXT
+
+// Entry states of the parts from the part summaries (groups, P - 1, N + 1, 64)
+// into entry (groups, P, N, 64): h0 (init, or 0) folded through the summaries
+// of the earlier parts; with reverse = 1, from the right (the backward's
+// adjoint, init = dh_last).
+hipError_t launch_fwd_carry(const float *summ, const float *init, const float *A, float *entry,
+                            int64_t batch, int64_t dim, int64_t N, int parts, int reverse,
+                            hipStream_t stream);
 
 // Forward part summaries alone (the summary pass of the streaming forward,
 // default instantiation) into summ: (groups, parts - 1, N + 1, 64) fp32.
