@@ -1,7 +1,7 @@
 """CPU oracle for the S6 selective scan -- test infrastructure only.
 
-Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
-``bench.py`` may import this package.  It shares no code with the HIP library.
+Only ``tests/``, the smoke check of the build entry point and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with the HIP library.
 
 ``selscan_oracle.c`` is the sequential fp64 definition of the scan (see its
 header for the page citations).  ``build()`` compiles it with gcc + OpenMP;
