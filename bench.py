@@ -16,7 +16,7 @@ last-level cache.
 
 The JSON line carries:
   value      elements (batch*L*dim) per second over the timed steps;
-  roofline   the forward call (summary pass + main pass) against the VALU
+  roofline   the forward call (summary, carry and main passes) against the VALU
              roofline: the path is bound by fp32 vector arithmetic, not by HBM
              (see algorithmic_valu_slots).  The call's average duration comes
              from HIP events recorded on the launch stream around each call;
@@ -498,7 +498,7 @@ def main():
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
                      "unit": "G VALU lane-slots/s", "frac": achieved / peak,
                      "traffic": load_traffic(w.name),
-                     "kernel": "selscan_fwd call (summary pass + main pass)",
+                     "kernel": "selscan_fwd call (summary, carry and main passes)",
                      "algorithmic_slots_per_element": algorithmic_valu_slots(w.N, w.gate, es),
                      "algorithmic_bytes_per_call": abytes,
                      "hbm_gbps_of_call": abytes / (call_mean * 1e-3) / 1e9},
