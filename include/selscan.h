@@ -100,7 +100,9 @@ enum selscan_status {
     SELSCAN_ERR_SHAPE = 2,       /* a size is < 1, or an element count overflows     */
     SELSCAN_ERR_DTYPE = 3,       /* dtype is neither SELSCAN_F32 nor SELSCAN_BF16    */
     SELSCAN_ERR_UNSUPPORTED = 4, /* N not in the compiled set, dim > 2^24 (forward),
-                                    or a pointer that is not 16-byte aligned         */
+                                    a launch grid past 2^31 - 1 workgroups (see
+                                    selscan_fwd), or a pointer that is not 16-byte
+                                    aligned                                          */
     SELSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
     SELSCAN_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer        */
     SELSCAN_ERR_HIP = 7          /* a HIP runtime call failed                        */
@@ -145,7 +147,9 @@ size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_
  *   stream                              hipStream_t as void*
  *
  * Required: batch, L, dim >= 1; dim <= 2^24; N supported; u, delta, A, Bm, Cm,
- * y non-NULL.
+ * y non-NULL; batch * ceil(dim/64) * max(ceil(L/16), N) < 2^31 (every launch
+ * grid fits; far beyond any shape whose arrays fit in device memory).  The
+ * workspace-size functions return 0 for shapes that violate these.
  */
 int selscan_fwd(const void *u, const void *delta, const float *A,
                 const void *Bm, const void *Cm, const float *D_skip,

@@ -26,6 +26,19 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // forward kernels within 32 bits (at most 16 timesteps x dim x 4 bytes < 2^30).
 const int64_t kMaxDim = (int64_t)1 << 24;
 
+// Every launch grid fits in 2^31 - 1 workgroups: the largest are one wave
+// per (channel group, sequence part), parts <= ceil(L/16), and the carry
+// kernel's N/4 workgroups per channel group.  (No shape whose arrays fit in
+// device memory comes near this; the check keeps a larger one from being
+// launched with a truncated grid.)
+bool grids_fit(int64_t batch, int64_t L, int64_t dim, int64_t N)
+{
+    const int64_t groups = batch * ((dim + 63) / 64);
+    const int64_t parts = (L + 15) / 16;
+    const int64_t per_group = parts > N ? parts : N;
+    return groups <= ((int64_t)1 << 31) / (per_group > 0 ? per_group : 1) - 1;
+}
+
 // Forward plans.  Default: the two-pass streaming kernel.  SELSCAN_FORCE_PLAN
 // = lookback selects the single-pass streaming kernel with decoupled
 // look-back; = chunked or = serial the workgroup-chunked or the
@@ -101,7 +114,7 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
         return SELSCAN_ERR_SHAPE;
     if (!u || !delta || !A || !Bm || !Cm || !y)
         return SELSCAN_ERR_NULL;
-    if (!supported_n(N) || dim > kMaxDim)
+    if (!supported_n(N) || dim > kMaxDim || !grids_fit(batch, L, dim, N))
         return SELSCAN_ERR_UNSUPPORTED;
     const float *conv_w = ext && ext->conv_k > 0 ? ext->conv_w : nullptr;
     const float *conv_b = ext && ext->conv_k > 0 ? ext->conv_b : nullptr;
@@ -169,7 +182,7 @@ int bwd_common(const void *u, const void *delta, const float *A, const void *Bm,
     if (!u || !delta || !A || !Bm || !Cm || !dy || !du || !ddelta || !dA || !dB || !dC ||
         (z && !dz))
         return SELSCAN_ERR_NULL;
-    if (!supported_n(N) || dim > kMaxDim)
+    if (!supported_n(N) || dim > kMaxDim || !grids_fit(batch, L, dim, N))
         return SELSCAN_ERR_UNSUPPORTED;
     if (!z)
         dz = nullptr;
@@ -250,7 +263,8 @@ int selscan_supports_n(int64_t N) { return supported_n(N) ? 1 : 0; }
 size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype)
 {
     if ((dtype != SELSCAN_F32 && dtype != SELSCAN_BF16) || !supported_n(N) ||
-        checked_count(batch, L, dim) < 0 || checked_count(batch, L, N) < 0)
+        checked_count(batch, L, dim) < 0 || checked_count(batch, L, N) < 0 ||
+        !grids_fit(batch, L, dim, N))
         return 0;
     const size_t a = selscan::fwd_chunked_workspace_bytes(batch, L, dim, N);
     const size_t b = selscan::fwd_stream_workspace_bytes(batch, L, dim, N);
@@ -294,7 +308,8 @@ int selscan_fwd_ex(const void *u, const void *delta, const float *A, const void 
 size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype)
 {
     if ((dtype != SELSCAN_F32 && dtype != SELSCAN_BF16) || !supported_n(N) ||
-        checked_count(batch, L, dim) < 0 || checked_count(batch, L, N) < 0 || dim > kMaxDim)
+        checked_count(batch, L, dim) < 0 || checked_count(batch, L, N) < 0 || dim > kMaxDim ||
+        !grids_fit(batch, L, dim, N))
         return 0;
     return selscan::bwd_workspace_bytes(batch, L, dim, N);
 }

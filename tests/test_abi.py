@@ -99,6 +99,8 @@ INVALID_FWD = [
     ("N5", dict(N=5), ERR_UNSUP),
     ("N128", dict(N=128), ERR_UNSUP),
     ("dim_too_large", dict(dim=(1 << 24) + 64, batch=1, L=2), ERR_UNSUP),
+    # 2^24 channel groups x 4096 sequence parts: a launch grid past 2^31 - 1
+    ("grid_too_large", dict(batch=1 << 20, L=1 << 16, dim=1 << 10), ERR_UNSUP),
     ("misaligned_u", dict(u=ctypes.c_void_p(BASE + STEP + 2)), ERR_UNSUP),
     ("misaligned_hlast", dict(h_last=ctypes.c_void_p(BASE + 11 * STEP + 8)), ERR_UNSUP),
     ("y_aliases_u", dict(y=ctypes.c_void_p(BASE + STEP + 64)), ERR_ALIAS),
@@ -205,6 +207,7 @@ INVALID_BWD = [
     ("dz_null_with_z", dict(dz=None), ERR_NULL),
     ("N12", dict(N=12), ERR_UNSUP),
     ("dim_too_large", dict(dim=(1 << 24) + 64, batch=1, L=2), ERR_UNSUP),
+    ("grid_too_large", dict(batch=1 << 20, L=1 << 16, dim=1 << 10), ERR_UNSUP),
     ("misaligned_dy", dict(dy=ctypes.c_void_p(BASE + 10 * STEP + 4)), ERR_UNSUP),
     ("misaligned_dh0", dict(dh0=ctypes.c_void_p(BASE + 20 * STEP + 8)), ERR_UNSUP),
     ("no_workspace", dict(workspace=None), ERR_WS),
@@ -264,6 +267,14 @@ def test_bwd_ex_rejects_invalid_arguments(name, kw, status):
     L = ss.lib()
     assert L.selscan_bwd_ex(*bwd_ex_args(**kw)) == status
     assert L.selscan_last_hip_error() == 0
+
+
+def test_workspace_size_zero_when_grids_do_not_fit():
+    L = ss.lib()
+    assert L.selscan_fwd_workspace_bytes(1 << 20, 1 << 16, 1 << 10, 16, 1) == 0
+    assert L.selscan_bwd_workspace_bytes(1 << 20, 1 << 16, 1 << 10, 16, 1) == 0
+    # the largest dim with a long sequence still fits
+    assert L.selscan_fwd_workspace_bytes(1, 1 << 17, 1 << 14, 16, 1) > 0
 
 
 def test_bwd_workspace_size():
