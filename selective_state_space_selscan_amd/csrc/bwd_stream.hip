@@ -66,6 +66,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N)
     w.asumm = off; off = align256(off + summ);
     w.fentry = off; off = align256(off + entry);
     w.aentry = off; off = align256(off + entry);
+    w.carry = off; off = align256(off + carry_scratch_bytes(w.p.groups, w.p.parts, N));
     w.ckpt = off; off = align256(off + (size_t)w.p.groups * w.nck * N * kLanes * 4);
     w.pB = off; off = align256(off + (size_t)w.gpr * batch * L * N * 4);
     w.pC = off; off = align256(off + (size_t)w.gpr * batch * L * N * 4);

@@ -801,8 +801,8 @@ hipError_t launch_colsum(const float *in, float *out, int64_t P, int64_t K, hipS
 struct BwdLayout {
     StreamPlan p;
     int64_t nck, gpr;
-    size_t fsumm, asumm, fentry, aentry, ckpt, pB, pC, pA, pD, pbias, pW, pWb, xown, xcarry,
-        total;   // byte offsets
+    size_t fsumm, asumm, fentry, aentry, carry, ckpt, pB, pC, pA, pD, pbias, pW, pWb, xown,
+        xcarry, total;   // byte offsets
 };
 BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N);
 
@@ -846,10 +846,11 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
         // entry states of the parts: h0 from the left, dh_last from the right
+        float *cscr = (float *)(base + w.carry);   // shared: the two carries run in turn
         if ((err = launch_fwd_carry(fsumm, a.fwd.h0, a.fwd.A, fentry, a.fwd.batch, a.fwd.dim, N,
-                                    p.parts, 0, s)) != hipSuccess ||
+                                    p.parts, 0, cscr, s)) != hipSuccess ||
             (err = launch_fwd_carry(asumm, a.dh_last, a.fwd.A, aentry, a.fwd.batch, a.fwd.dim, N,
-                                    p.parts, 1, s)) != hipSuccess)
+                                    p.parts, 1, cscr, s)) != hipSuccess)
             return err;
     }
     const bool split = p.parts > 1;

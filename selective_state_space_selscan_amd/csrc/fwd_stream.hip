@@ -56,7 +56,8 @@ size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t
         return 0;
     const size_t summ = (size_t)p.groups * (p.parts - 1) * (N + 1) * stream::kLanes * 4;
     const size_t entry = (size_t)p.groups * p.parts * N * stream::kLanes * 4;
-    return 256 + ((summ + 255) & ~(size_t)255) + entry;
+    return 256 + ((summ + 255) & ~(size_t)255) + ((entry + 255) & ~(size_t)255) +
+           carry_scratch_bytes(p.groups, p.parts, N);
 }
 
 namespace {
@@ -121,29 +122,146 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ su
     }
 }
 
+// Two-level carry for many parts: the summaries are taken in blocks of
+// kCarryBlock; the blocks' aggregates (decay sum and end state from zero, the
+// summary of the whole block) are folded by carry_kernel, and each block's
+// entries then filled from its carried start.  The sequential depth drops
+// from P to about 2 kCarryBlock + P / kCarryBlock.
+constexpr int kCarryBlock = 64;
+
+__host__ __device__ inline int64_t carry_blocks(int parts)
+{
+    return (parts - 1 + kCarryBlock - 1) / kCarryBlock;
+}
+
+// fill = false: the aggregate of block blk into bsumm (groups, nb, N + 1, 64),
+// in the fold's order (from the right with reverse).  fill = true: the block's
+// entries, folded from bentry (groups, nb + 1, N, 64, from carry_kernel) into
+// entry.  One lane per (group, block, n, channel).
+template <int N>
+__global__ __launch_bounds__(256) void carry_block_kernel(const float *__restrict__ summ,
+                                                          const float *__restrict__ A,
+                                                          float *__restrict__ bsumm,
+                                                          const float *__restrict__ bentry,
+                                                          float *__restrict__ entry,
+                                                          const float *__restrict__ init,
+                                                          int64_t dim, int64_t groups, int parts,
+                                                          int reverse, int fill)
+{
+    constexpr int kLanes = stream::kLanes;
+    const int64_t nb = carry_blocks(parts);
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = (int)(tid & (kLanes - 1));
+    int64_t w = tid / kLanes;   // (group, block, n), wave-uniform
+    if (w >= groups * nb * N)
+        return;
+    const int n = (int)(w % N);
+    w /= N;
+    const int64_t blk = w % nb;
+    const int64_t grp = w / nb;
+    const int64_t gpr = (dim + kLanes - 1) / kLanes;
+    const int64_t d0 = (grp % gpr) * kLanes;
+    const int64_t d = d0 + lane < dim ? d0 + lane : dim - 1;
+    const float a2 = A[d * N + n] * kLog2e;
+    const int J = parts - 1;
+    const int j_lo = (int)(blk * kCarryBlock);
+    const int j_hi = j_lo + kCarryBlock < J ? j_lo + kCarryBlock : J;
+    const int cnt = j_hi - j_lo;
+    const int64_t sstride = (int64_t)(N + 1) * kLanes;
+    const int64_t estride = (int64_t)N * kLanes;
+    const float *sb = summ + grp * (parts - 1) * sstride + lane;
+    float *eb = entry + grp * parts * estride + n * kLanes + lane;
+    const float *be = bentry + (grp * (nb + 1)) * estride + n * kLanes + lane;
+    float h = 0.0f, S = 0.0f;
+    if (fill) {
+        // state before the block: from the left E[j_lo], from the right E[j_hi]
+        h = be[(reverse ? blk + 1 : blk) * estride];
+        if (!reverse && blk == 0)
+            eb[0] = h;
+        if (reverse && blk == nb - 1)
+            eb[(int64_t)J * estride] = h;
+    }
+    for (int k0 = 0; k0 < cnt; k0 += kCarryBatch) {
+        float Sv[kCarryBatch], X[kCarryBatch];
+#pragma unroll
+        for (int k = 0; k < kCarryBatch; ++k) {
+            const int j = reverse ? j_hi - 1 - (k0 + k) : j_lo + k0 + k;
+            const bool in = k0 + k < cnt;
+            Sv[k] = in ? sb[j * sstride] : 0.0f;
+            X[k] = in ? sb[j * sstride + (n + 1) * kLanes] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kCarryBatch; ++k) {
+            if (k0 + k < cnt) {
+                const int j = reverse ? j_hi - 1 - (k0 + k) : j_lo + k0 + k;
+                h = fmaf(hw_exp2(a2 * Sv[k]), h, X[k]);
+                S += Sv[k];
+                if (fill)
+                    eb[(reverse ? j : j + 1) * estride] = h;
+            }
+        }
+    }
+    if (!fill) {
+        float *o = bsumm + (grp * nb + blk) * sstride + lane;
+        if (n == 0)
+            o[0] = S;
+        o[(n + 1) * kLanes] = h;
+    }
+    (void)init;
+}
+
 template <int N>
 hipError_t carry_n(const float *summ, const float *init, const float *A, float *entry,
-                   int64_t batch, int64_t dim, int parts, int reverse, hipStream_t s)
+                   int64_t batch, int64_t dim, int parts, int reverse, float *scratch,
+                   hipStream_t s)
 {
     const int64_t groups = batch * ((dim + stream::kLanes - 1) / stream::kLanes);
-    const int64_t threads = groups * N * stream::kLanes;
-    hipLaunchKernelGGL((carry_kernel<N>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, summ, init, A, entry, dim, groups, parts, reverse);
+    const int64_t nb = carry_blocks(parts);
+    if (!scratch || nb <= 2) {
+        const int64_t threads = groups * N * stream::kLanes;
+        hipLaunchKernelGGL((carry_kernel<N>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                           0, s, summ, init, A, entry, dim, groups, parts, reverse);
+        return hipGetLastError();
+    }
+    float *bsumm = scratch;
+    float *bentry = scratch + groups * nb * (N + 1) * stream::kLanes;
+    const int64_t threads = groups * nb * N * stream::kLanes;
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    hipLaunchKernelGGL((carry_block_kernel<N>), grid, block, 0, s, summ, A, bsumm,
+                       (const float *)nullptr, entry, init, dim, groups, parts, reverse, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t t2 = groups * N * stream::kLanes;
+    hipLaunchKernelGGL((carry_kernel<N>), dim3((unsigned)((t2 + 255) / 256)), dim3(256), 0, s,
+                       (const float *)bsumm, init, A, bentry, dim, groups, (int)nb + 1, reverse);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((carry_block_kernel<N>), grid, block, 0, s, summ, A, (float *)nullptr,
+                       (const float *)bentry, entry, init, dim, groups, parts, reverse, 1);
     return hipGetLastError();
 }
 
 } // namespace
 
+size_t carry_scratch_bytes(int64_t groups, int parts, int64_t N)
+{
+    const int64_t nb = carry_blocks(parts);
+    if (parts <= 1 || nb <= 2)
+        return 0;
+    return (size_t)groups * (nb * (N + 1) + (nb + 1) * N) * stream::kLanes * 4;
+}
+
 hipError_t launch_fwd_carry(const float *summ, const float *init, const float *A, float *entry,
                             int64_t batch, int64_t dim, int64_t N, int parts, int reverse,
-                            hipStream_t stream)
+                            float *scratch, hipStream_t stream)
 {
     switch (N) {
-    case 4: return carry_n<4>(summ, init, A, entry, batch, dim, parts, reverse, stream);
-    case 8: return carry_n<8>(summ, init, A, entry, batch, dim, parts, reverse, stream);
-    case 16: return carry_n<16>(summ, init, A, entry, batch, dim, parts, reverse, stream);
-    case 32: return carry_n<32>(summ, init, A, entry, batch, dim, parts, reverse, stream);
-    case 64: return carry_n<64>(summ, init, A, entry, batch, dim, parts, reverse, stream);
+    case 4: return carry_n<4>(summ, init, A, entry, batch, dim, parts, reverse, scratch, stream);
+    case 8: return carry_n<8>(summ, init, A, entry, batch, dim, parts, reverse, scratch, stream);
+    case 16: return carry_n<16>(summ, init, A, entry, batch, dim, parts, reverse, scratch, stream);
+    case 32: return carry_n<32>(summ, init, A, entry, batch, dim, parts, reverse, scratch, stream);
+    case 64: return carry_n<64>(summ, init, A, entry, batch, dim, parts, reverse, scratch, stream);
     default: return hipErrorInvalidValue;
     }
 }

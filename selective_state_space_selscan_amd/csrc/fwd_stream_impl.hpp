@@ -676,6 +676,25 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
     }
 }
 
+inline float *summary_buffer(void *workspace)
+{
+    return (float *)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+}
+
+// Entry states after the summaries: (groups, parts, N, 64) fp32.
+inline float *entry_buffer(void *workspace, const StreamPlan &p, int64_t N)
+{
+    const size_t summ = (size_t)p.groups * (p.parts > 1 ? p.parts - 1 : 0) * (N + 1) * kLanes * 4;
+    return (float *)((char *)summary_buffer(workspace) + ((summ + 255) & ~(size_t)255));
+}
+
+// The two-level carry's block buffers, after the entry states.
+inline float *carry_scratch(void *workspace, const StreamPlan &p, int64_t N)
+{
+    const size_t entry = (size_t)p.groups * p.parts * N * kLanes * 4;
+    return (float *)((char *)entry_buffer(workspace, p, N) + ((entry + 255) & ~(size_t)255));
+}
+
 // Summary pass (when the sequence is split), then the main pass, on one stream.
 template <int N, int VAR, typename TIO>
 hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p, float *summ,
@@ -695,7 +714,8 @@ hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p,
         if (e != hipSuccess)
             return e;
         if (entry) {
-            e = launch_fwd_carry(summ, a.h0, a.A, entry, a.batch, a.dim, N, p.parts, 0, s);
+            e = launch_fwd_carry(summ, a.h0, a.A, entry, a.batch, a.dim, N, p.parts, 0,
+                                 carry_scratch(a.workspace, p, N), s);
             if (e != hipSuccess)
                 return e;
         }
@@ -740,18 +760,6 @@ hipError_t launch_ext_summaries(const FwdArgs &a, const FwdExt &e, const StreamP
     }
 #undef SELSCAN_SUMM
     return hipGetLastError();
-}
-
-inline float *summary_buffer(void *workspace)
-{
-    return (float *)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
-}
-
-// Entry states after the summaries: (groups, parts, N, 64) fp32.
-inline float *entry_buffer(void *workspace, const StreamPlan &p, int64_t N)
-{
-    const size_t summ = (size_t)p.groups * (p.parts > 1 ? p.parts - 1 : 0) * (N + 1) * kLanes * 4;
-    return (float *)((char *)summary_buffer(workspace) + ((summ + 255) & ~(size_t)255));
 }
 
 // Variant forward for one N and one B_bar form (ZOH: exact zero-order hold):

@@ -100,9 +100,12 @@ SELSCAN_DECLARE_EXT(64)
 // into entry (groups, P, N, 64): h0 (init, or 0) folded through the summaries
 // of the earlier parts; with reverse = 1, from the right (the backward's
 // adjoint, init = dh_last).
+// scratch: carry_scratch_bytes(groups, parts, N) bytes for the two-level carry
+// of many parts (null: the single-level carry).
 hipError_t launch_fwd_carry(const float *summ, const float *init, const float *A, float *entry,
                             int64_t batch, int64_t dim, int64_t N, int parts, int reverse,
-                            hipStream_t stream);
+                            float *scratch, hipStream_t stream);
+size_t carry_scratch_bytes(int64_t groups, int parts, int64_t N);
 
 // Forward part summaries alone (the summary pass of the streaming forward,
 // default instantiation) into summ: (groups, parts - 1, N + 1, 64) fp32.

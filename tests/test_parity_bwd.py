@@ -127,3 +127,11 @@ def test_bwd_layer_workload(device):
     w = si.WORKLOADS["mamba130m_layer"]
     inp = si.workload_fwd_inputs(w)
     check_bwd(inp, device, 1300, "mamba130m_layer", with_dh_last=False)
+
+
+def test_bwd_long_sequence_many_parts(device):
+    """One channel group over a long sequence: 512 parts, so the entry states
+    come from the two-level carry (blocks of 64 part summaries), in both
+    directions (h0 from the left, dh_last from the right)."""
+    inp = si.make_fwd_inputs(1, 8192, 64, 16, si.F32, True, seed=1310, h0=True)
+    check_bwd(inp, device, 1311, "long/many parts")

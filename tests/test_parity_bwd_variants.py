@@ -219,3 +219,10 @@ def test_bwd_variants_layer_workload(device, flags):
     inp = si.workload_fwd_inputs(w)
     check_bwd_ex(inp, device, 1550 + flags, flags, si.conv_params(w.dim, 4, 1551),
                  what="mamba130m_layer", with_dh_last=False)
+
+
+def test_bwd_variants_long_sequence_many_parts(device):
+    """512 parts on one channel group (the two-level carry), with exact ZOH,
+    reverse and the conv prologue."""
+    inp = si.make_fwd_inputs(1, 8192, 64, 16, si.F32, True, seed=1560, h0=True)
+    check_bwd_ex(inp, device, 1561, ZOH | REV, si.conv_params(64, 4, 1562), what="long")
