@@ -18,13 +18,18 @@ The JSON line carries:
   value      elements (batch*L*dim) per second over the timed steps;
   roofline   the forward call (summary, carry and main passes) against the VALU
              roofline: the path is bound by fp32 vector arithmetic, not by HBM
-             (see algorithmic_valu_slots).  The call's average duration comes
-             from HIP events recorded on the launch stream around each call;
+             (see algorithmic_valu_slots).  The call's average duration is
+             the interval between two HIP events recorded on the launch
+             stream around the timed steps, divided by their number;
+  call_ms    that average, and the spread of single calls timed afterwards
+             (50 more calls, each between its own pair of events);
   traffic    HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
              scaled by the same counters on a plain 1 GiB copy, read from
              profiles/traffic_<workload>.json if the kernel sources are
              unchanged since it was taken, else null;
   hbm_*      algorithmic bytes per call / step time, against the 8 TB/s peak;
+  device_copy_gbps  a plain 512 MiB device copy timed in the same run, for
+             context (what HBM delivers to a copy on this box);
   cpu_baseline  the CPU oracle (fp64, OpenMP) on a bounded sample.
 """
 from __future__ import annotations
@@ -270,6 +275,7 @@ def bench_decode(w, steps, warmup):
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "N": w.N,
                    "state": "fp32 resident"},
         "step_ms_warm": warm_ms, "step_ms_cold": cold_ms,
+        "device_copy_gbps": device_copy_gbps(dev),
         "roofline": {"bound": "hbm", "achieved": nb / (cold_ms * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": nb / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
@@ -278,6 +284,61 @@ def bench_decode(w, steps, warmup):
                      "warm_gbps": nb / (warm_ms * 1e-3) / 1e9},
     }
     print(json.dumps(res), flush=True)
+
+
+def timed_steps(step, steps, warmup, stream, percall=50):
+    """``warmup`` untimed steps, then exactly ``steps`` steps back to back,
+    bracketed by a synchronize on both sides (host clock) and by one pair of
+    HIP events on the launch stream (device clock): the average call
+    duration is the event interval / ``steps``.  Then ``percall`` further
+    steps, each between its own pair of events, for the spread of single
+    calls; they are not part of the timed region (an event pair per call
+    adds a small bubble of its own).  Returns (wall s, mean call ms,
+    per-call ms array)."""
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_mean = a.elapsed_time(b) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(percall)]
+    for i, (x, y) in enumerate(ev):
+        x.record(stream)
+        step(warmup + steps + i)
+        y.record(stream)
+    torch.cuda.synchronize()
+    return wall, call_mean, np.array([x.elapsed_time(y) for x, y in ev])
+
+
+def device_copy_gbps(dev, nbytes=1 << 29, reps=10):
+    """Same-run context for the HBM figures: a device-to-device copy of
+    ``nbytes`` (read + write counted), median over ``reps`` copies timed with
+    HIP events, after the workload's own timing."""
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del src, dst
+    return 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
 
 
 def bwd_valu_slots(N, gate, es):
@@ -315,7 +376,7 @@ def bench_bwd(w, args):
         cw, cb = si.conv_params(w.dim, vconv, w.seed)
         conv_w, conv_b = torch.from_numpy(cw).to(dev), torch.from_numpy(cb).to(dev)
 
-    def step():
+    def step(i):
         if args.variant:
             ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"],
                               t["z"], t["delta_bias"], True, None, None, flags=vflags,
@@ -324,22 +385,9 @@ def bench_bwd(w, args):
         ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"], t["z"],
                        t["delta_bias"], True, None, None, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    wall, call_mean, call_ms = timed_steps(step, args.steps, args.warmup, stream)
     es = 2 if w.dtype == si.BF16 else 4
     elems = w.batch * w.L * w.dim
-    call_mean = float(np.mean(call_ms))
     slots = bwd_valu_slots(w.N, w.gate, es) * elems
     # bytes the backward must move: the forward's inputs once, dy, and the
     # gradients du, ddelta, dz (dtype) and dB, dC (fp32) once
@@ -354,7 +402,7 @@ def bench_bwd(w, args):
         "dtype": "bf16" if w.dtype == si.BF16 else "f32", "data": "synthetic (seeded)",
         "config": {"workload": w.name, "pass": "bwd", "batch": w.batch, "L": w.L, "dim": w.dim,
                    "N": w.N, "gate": w.gate},
-        "call_ms": {"mean": call_mean, "p50": float(np.median(call_ms))},
+        "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms))},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_SLOTS / 1e9,
                      "unit": "G VALU lane-slots/s", "frac": achieved * 1e9 / VALU_PEAK_SLOTS,
                      "traffic": None, "kernel": "selscan_bwd call (all passes)",
@@ -387,7 +435,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first: about 0.1 s of work, so that the clocks have "
+                         "ramped up before the timed region")
     ap.add_argument("--workload", default="mamba130m_layer")
     ap.add_argument("--rotate", type=int, default=4, help="input-set copies to rotate")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -452,24 +502,10 @@ def main():
                        y=ys[i % args.rotate], h_last=hls[i % args.rotate],
                        workspace=wss[i % args.rotate], stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(args.warmup + i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    call_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    wall, call_mean, call_ms = timed_steps(step, args.steps, args.warmup, stream)
 
     elems = w.batch * w.L * w.dim
     ms_per_step = 1e3 * wall / args.steps
-    call_mean = float(np.mean(call_ms))
     abytes = algorithmic_bytes(w.batch, w.L, w.dim, w.N, es, w.gate, w.want_last_state)
     slots = algorithmic_valu_slots(w.N, w.gate, es) * elems
     achieved = slots / (call_mean * 1e-3) / 1e9
@@ -493,8 +529,11 @@ def main():
         **({"variant": args.variant} if args.variant else {}),
         "hbm_gbps": abytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": abytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "call_ms": {"mean": call_mean, "p10": float(np.percentile(call_ms, 10)),
-                    "p50": float(np.median(call_ms)), "p90": float(np.percentile(call_ms, 90))},
+        "call_ms": {"mean": call_mean,
+                    "single_call": {"p10": float(np.percentile(call_ms, 10)),
+                                    "p50": float(np.median(call_ms)),
+                                    "p90": float(np.percentile(call_ms, 90)),
+                                    "calls": len(call_ms)}},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
                      "unit": "G VALU lane-slots/s", "frac": achieved / peak,
                      "traffic": load_traffic(w.name),
@@ -507,6 +546,7 @@ def main():
         result["roofline"]["traffic"] = None
         result["roofline"]["kernel"] = "selscan_fwd_ex call (%s); slots of the default path" \
             % args.variant
+    result["device_copy_gbps"] = device_copy_gbps(dev)
     if not args.no_cpu and not args.variant:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)
