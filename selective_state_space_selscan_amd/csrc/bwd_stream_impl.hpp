@@ -65,6 +65,7 @@ using stream::kLanes;
 using stream::kMaxConv;
 using stream::kVarConv;
 using stream::kVarExt;
+using stream::kVarRev;
 using stream::kVarZoh;
 using stream::RowRaw;
 using stream::TT;
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_pass23_kernel(
     }
     if constexpr ((ROLES & 1) != 0) {
         if (is_adj) {
-            adjoint_summary_wave<N, VAR == 0 ? 0 : (int)kVarExt, TIO>(
+            adjoint_summary_wave<N, (VAR & ~kVarRev) == 0 ? VAR : (int)kVarExt, TIO>(
                 delta, z, dy, A, Cm, delta_bias, delta_softplus, asumm, ext.rev, idx, L, dim,
                 groups, parts, part_len);
             return;
@@ -456,15 +457,19 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
     // faster one (fewer scalar-register spills, measured) for its case: with
     // the direction fixed at compile time, rows and inputs are formed at use;
     // with a run-time direction, from a row base and step computed once.
+    // (kVarRev: the fixed direction is the reverse one.)
     constexpr bool FIXED = (VAR & kVarExt) == 0;
+    constexpr bool REVF = (VAR & kVarRev) != 0;
     const int rows = (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
     const int64_t row0 = scan_row<VAR>(c, t0);
     const int64_t dir = row_dir<VAR>(c);
     auto step_row = [&](int i, bool valid) -> int64_t {
-        if constexpr (FIXED)
-            return c.bL + (valid ? t0 + i : t0);
-        else
+        if constexpr (FIXED) {
+            const int64_t st = valid ? t0 + i : t0;
+            return c.bL + (REVF ? c.L - 1 - st : st);
+        } else {
             return valid ? row0 + i * dir : row0;
+        }
     };
     // scan inputs of the TT steps; with the conv prologue, the raw inputs of
     // steps t0-kHalo .. t0+TT-1 (xw[j] is step t0-kHalo+j) and the
@@ -647,7 +652,8 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
         }
         __syncthreads();
         if (lane < N && valid) {
-            const int64_t t = FIXED ? t0 + i : row - c.bL;   // timestep of the step
+            const int64_t t = FIXED ? (REVF ? c.L - 1 - (t0 + i) : t0 + i)
+                                    : row - c.bL;   // timestep of the step
             const int64_t off = ((grp_in_row * batch + c.b) * c.L + t) * N + lane;
             o.pB[off] = sb;
             o.pC[off] = sc;
@@ -899,7 +905,7 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
                                         a.fwd.dim, N, p.parts, 1, cscr, s)
                      : hipSuccess;
     };
-    if constexpr (VAR == 0) {
+    if constexpr ((VAR & ~kVarRev) == 0) {
         // the checkpoints need the forward entry states
         if ((err = carry_fwd()) != hipSuccess)
             return err;

@@ -68,7 +68,10 @@ constexpr int TTS = 8;  // timesteps per prefetch buffer, summary pass
 constexpr int kStoreOffsetOutOfRange = 1 << 30;
 static_assert(TT <= kStreamTT, "plan rounds parts to kStreamTT steps");
 
-enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4 };
+// kVarRev: reverse direction fixed at compile time, used alone (no kVarExt):
+// the reverse-only call then compiles to the default's code with the
+// addressing mirrored.
+enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4, kVarRev = 8 };
 constexpr int kMaxConv = 4;
 
 // Variant arguments of the kernel (ignored when VAR = 0).
@@ -101,7 +104,9 @@ struct WaveCtx {
 template <int VAR>
 __device__ __forceinline__ int64_t scan_row(const WaveCtx &c, int64_t s)
 {
-    if constexpr ((VAR & kVarExt) != 0)
+    if constexpr ((VAR & kVarRev) != 0)
+        return c.bL + c.L - 1 - s;
+    else if constexpr ((VAR & kVarExt) != 0)
         return c.bL + (c.rev ? c.L - 1 - s : s);
     else
         return c.bL + s;
@@ -111,7 +116,9 @@ __device__ __forceinline__ int64_t scan_row(const WaveCtx &c, int64_t s)
 template <int VAR>
 __device__ __forceinline__ int64_t row_dir(const WaveCtx &c)
 {
-    if constexpr ((VAR & kVarExt) != 0)
+    if constexpr ((VAR & kVarRev) != 0)
+        return -1;
+    else if constexpr ((VAR & kVarExt) != 0)
         return c.rev ? -1 : 1;
     else
         return 1;
@@ -124,7 +131,9 @@ __device__ __forceinline__ int64_t row_dir(const WaveCtx &c)
 template <int VAR>
 __device__ __forceinline__ int64_t run_t_lo(const WaveCtx &c, int64_t s0, int64_t rows)
 {
-    if constexpr ((VAR & kVarExt) != 0)
+    if constexpr ((VAR & kVarRev) != 0)
+        return c.L - s0 - rows;
+    else if constexpr ((VAR & kVarExt) != 0)
         return c.rev ? c.L - s0 - rows : s0;
     else
         return s0;
@@ -132,7 +141,9 @@ __device__ __forceinline__ int64_t run_t_lo(const WaveCtx &c, int64_t s0, int64_
 template <int VAR>
 __device__ __forceinline__ int step_soff(const WaveCtx &c, int i, int rows)
 {
-    if constexpr ((VAR & kVarExt) != 0) {
+    if constexpr ((VAR & kVarRev) != 0) {
+        return i < rows ? (rows - 1 - i) * c.row_bytes : kStoreOffsetOutOfRange;
+    } else if constexpr ((VAR & kVarExt) != 0) {
         if (c.rev)
             return i < rows ? (rows - 1 - i) * c.row_bytes : kStoreOffsetOutOfRange;
     }
@@ -593,7 +604,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
     const bool active = c.d0 + lane < dim;
     const int64_t d = active ? c.d0 + lane : dim - 1;
     c.voff_store = active ? c.voff : kStoreOffsetOutOfRange;
-    c.rev = EXT ? ext.rev : 0;
+    c.rev = (VAR & kVarRev) != 0 ? 1 : EXT ? ext.rev : 0;
     c.softplus = delta_softplus;
 
     const float A0 = A[d * N];
@@ -768,9 +779,22 @@ template <int N, bool ZOH>
 hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
 {
     constexpr int V0 = kVarExt | (ZOH ? kVarZoh : 0);
+    float *summ = summary_buffer(a.workspace);
+    const bool bf = a.dtype == 1;
+    if constexpr (!ZOH) {
+        if (e.conv_k == 0 && (e.flags & kFwdFlagReverse)) {
+            // reverse alone: the default's plan, carry kernel and code with the
+            // addressing mirrored (157 -> 134..142 us on batch 8, L 2048,
+            // D 1536, N 16, against the run-time direction)
+            const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, 4, kDefaultFwdSlotsX2);
+            float *entry = entry_buffer(a.workspace, p, N);
+            ExtParams none{};
+            return bf ? launch_n<N, kVarRev, uint16_t>(a, none, p, summ, entry, s)
+                      : launch_n<N, kVarRev, float>(a, none, p, summ, entry, s);
+        }
+    }
     const int occupancy = e.conv_k > 0 ? waves_per_eu<N, V0 | kVarConv>() : waves_per_eu<N, V0>();
     const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, occupancy);
-    float *summ = summary_buffer(a.workspace);
     float *entry = nullptr;   // the variants fold the summaries in the main pass
     ExtParams x;
     x.conv_w = e.conv_k > 0 ? e.conv_w : nullptr;
@@ -778,7 +802,6 @@ hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
     x.conv_k = e.conv_k;
     x.rev = (e.flags & kFwdFlagReverse) ? 1 : 0;
     constexpr int V = kVarExt | (ZOH ? kVarZoh : 0);
-    const bool bf = a.dtype == 1;
     if (e.conv_k > 0)
         return bf ? launch_n<N, V | kVarConv, uint16_t>(a, x, p, summ, entry, s)
                   : launch_n<N, V | kVarConv, float>(a, x, p, summ, entry, s);

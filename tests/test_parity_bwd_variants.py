@@ -200,6 +200,26 @@ def test_bwd_reverse_is_forward_on_flipped_sequence_bitwise(device, flags, conv)
         assert torch.equal(g_r[k], other), k
 
 
+@pytest.mark.parametrize("N,dtype,shape", [
+    (4, si.F32, (2, 300, 96)), (8, si.BF16, (3, 517, 130)), (32, si.BF16, (2, 300, 96)),
+    (64, si.F32, (1, 250, 64)), (16, si.F32, (1, 8192, 64))])   # the last: 512 parts
+def test_bwd_reverse_alone_flipped_bitwise_every_size(device, N, dtype, shape):
+    """REVERSE without ZOH or conv (its own instantiation, direction fixed at
+    compile time) against the forward direction on the flipped inputs, bit
+    for bit, for every state size, both dtypes and the two-level carry."""
+    batch, L, dim = shape
+    inp = si.make_fwd_inputs(batch, L, dim, N, dtype, True, seed=1570 + N, h0=True)
+    say("case reverse alone", N, dtype, shape)
+    dy, dhl = upstream(inp, 1571 + N)
+    g_r = run_bwd_ex(inp, dy, dhl, device, REV, None)
+    g_f = run_bwd_ex(inp, dy, dhl, device, 0, None, flip=True)
+    for k in NAMES:
+        if g_r.get(k) is None:
+            continue
+        other = g_f[k].flip(1) if k in ("du", "ddelta", "dz", "dB", "dC") else g_f[k]
+        assert torch.equal(g_r[k], other), k
+
+
 def test_bwd_variants_bitwise_repeatable(device):
     inp = si.make_fwd_inputs(2, 1500, 200, 16, si.BF16, True, seed=1540, h0=True)
     dy, dhl = upstream(inp, 1541)
@@ -219,6 +239,9 @@ def test_bwd_variants_layer_workload(device, flags):
     inp = si.workload_fwd_inputs(w)
     check_bwd_ex(inp, device, 1550 + flags, flags, si.conv_params(w.dim, 4, 1551),
                  what="mamba130m_layer", with_dh_last=False)
+    if flags == REV:
+        check_bwd_ex(inp, device, 1553, flags, None, what="mamba130m_layer, reverse alone",
+                     with_dh_last=False)
 
 
 def test_bwd_variants_long_sequence_many_parts(device):

@@ -165,6 +165,29 @@ def test_reverse_is_forward_on_flipped_sequence_bitwise(device, dtype, conv):
     assert torch.equal(y_r, f(y_f)) and torch.equal(h_r, h_f)
 
 
+@pytest.mark.parametrize("N,dtype,shape", [
+    (16, si.BF16, (2, 1234, 192)), (16, si.F32, (3, 517, 130)), (4, si.BF16, (2, 700, 96)),
+    (8, si.F32, (1, 333, 64)), (32, si.BF16, (2, 300, 96)), (64, si.F32, (1, 250, 64)),
+    (16, si.BF16, (1, 1 << 17, 64))])   # the last: hundreds of parts, two-level carry
+def test_reverse_alone_is_default_forward_flipped_bitwise(device, N, dtype, shape):
+    """REVERSE without ZOH or conv runs the default forward's plan, carry and
+    arithmetic with mirrored addressing: bit for bit the default forward
+    (selscan_fwd) on the time-flipped inputs, y flipped back, same h_last."""
+    batch, L, dim = shape
+    inp = si.make_fwd_inputs(batch, L, dim, N, dtype, True, seed=1200 + N, h0=True)
+    print("case reverse alone", N, dtype, shape, flush=True)
+    t = si.fwd_tensors(inp, device)
+    f = lambda x: x.flip(1).contiguous()
+    y_r, h_r = ss.selscan_fwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"],
+                                 t["z"], t["delta_bias"], True, t["h0"], return_last_state=True,
+                                 flags=REV)
+    y_f, h_f = ss.selscan_fwd(f(t["u"]), f(t["delta"]), t["A"], f(t["Bm"]), f(t["Cm"]),
+                              t["D_skip"], f(t["z"]), t["delta_bias"], True, t["h0"],
+                              return_last_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_r, f(y_f)) and torch.equal(h_r, h_f)
+
+
 @pytest.mark.parametrize("flags", [ZOH | REV, REV])
 def test_variants_layer_workload(device, flags):
     """The 130M-layer shape (batch 8, L 2048, D 1536, N 16, bf16, gate) with
@@ -172,3 +195,5 @@ def test_variants_layer_workload(device, flags):
     w = si.WORKLOADS["mamba130m_layer"]
     inp = si.workload_fwd_inputs(w)
     check_ex(inp, device, flags, si.conv_params(w.dim, 4, 1100), what="mamba130m_layer")
+    if flags == REV:
+        check_ex(inp, device, flags, None, what="mamba130m_layer, reverse alone")
