@@ -194,7 +194,8 @@ def parse_pmc(w, fetch_dir, write_dir, reps=3):
         out[name] = {"counter": counter, "kib_per_call_raw": kib_per_call,
                      "copy_kib_raw": copy[0] if copy else None, "copy_factor": factor,
                      "bytes_per_call": None if factor is None else kib_per_call * 1024.0 * factor,
-                     "kernels": sorted({k.split("(")[0] for k, _ in scan})}
+                     "kernels": sorted({k.replace("(anonymous namespace)::", "").split("(")[0]
+                                        for k, _ in scan})}
     total = (out["fetch"]["bytes_per_call"] or 0) + (out["write"]["bytes_per_call"] or 0)
     res = {"workload": w.name, "source_sha256": source_digest(), "bytes_per_call": total,
            "fetch": out["fetch"], "write": out["write"],
