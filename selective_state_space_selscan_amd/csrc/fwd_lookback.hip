@@ -176,9 +176,9 @@ void fwd_lookback_kernel(const TIO *__restrict__ u, const TIO *__restrict__ delt
         c.Dd = 0.0f;
         if (pow_path) {
             if (delta_softplus)
-                summary_part_rev<N, true, 0>(u, delta, Bm, c, x, S);
+                summary_part_rev<N, true, 0>(u, delta, Bm, c, win, x, S);
             else
-                summary_part_rev<N, false, 0>(u, delta, Bm, c, x, S);
+                summary_part_rev<N, false, 0>(u, delta, Bm, c, win, x, S);
         } else {
             if (delta_softplus)
                 run_part<N, true, false, true, false, 0>(u, delta, z, y, Bm, Cm, c, A2, invA, x,

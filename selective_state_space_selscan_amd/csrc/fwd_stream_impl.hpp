@@ -393,14 +393,28 @@ __device__ __forceinline__ void run_part(const TIO *u, const TIO *delta, const T
 // Q_t = prod_{s>t} r_s and r_s = exp(Delta_s A[d,0]).  Walking backwards, Q
 // is one running product and Delta_t u_t Q_t^(n+1) one multiply per n, so a
 // (t, n) costs a multiply and an FMA (the forward walk needs three ops).
-// Not used with the exact-ZOH or conv variants (their input of a step is
-// not Delta_t u_t, or depends on the steps before it).
+// Not used with exact ZOH (its input of a step is not Delta_t u_t).  With the
+// conv prologue the input of step i needs the raw inputs of steps i-3..i:
+// inside the chunk, or for its first steps the last raw inputs of the chunk
+// before it (prev: the next chunk of the walk, prefetched while this one
+// computes, and needed only at the end of this one's walk) or, at the start
+// of the part, the window before the part (win).
 template <int N, bool SOFTPLUS, bool FULL, int VAR, typename TIO>
-__device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const TIO *Bm,
-                                                  const WaveCtx &c, int64_t t0, float &Q,
-                                                  float (&x)[N], float &sdelta)
+__device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const ChunkT<TTS> &prev,
+                                                  bool prev_in_part,
+                                                  const float (&win)[kMaxConv - 1],
+                                                  const TIO *Bm, const WaveCtx &c, int64_t t0,
+                                                  float &Q, float (&x)[N], float &sdelta)
 {
     constexpr int TT = TTS;
+    constexpr bool CONV = (VAR & kVarConv) != 0;
+    static_assert(TT >= kMaxConv - 1, "the conv window reaches one chunk back at most");
+    // raw input of chunk step j, j >= -(kMaxConv - 1)
+    auto raw_in = [&](int j) -> float {
+        if (j >= 0)
+            return raw_to_f32(ch.u[j], tag<TIO>());
+        return prev_in_part ? raw_to_f32(prev.u[TT + j], tag<TIO>()) : win[kMaxConv - 1 + j];
+    };
     const int rows = FULL ? TT : (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
     // B_t row of step i-1 is fetched (scalar loads) while step i computes.
     const int64_t row0 = scan_row<VAR>(c, t0);
@@ -413,7 +427,17 @@ __device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const T
             continue;   // uniform: steps past the end contribute nothing
         if (i > 0)
             fetch_row(bnxt, Bm, row0 + (i - 1) * dir);
-        const float ut = raw_to_f32(ch.u[i], tag<TIO>());
+        float ut;
+        if constexpr (CONV) {
+            // the main pass's step_input: the same FMAs in the same order
+            float acc = c.cb;
+#pragma unroll
+            for (int m = 0; m < kMaxConv; ++m)
+                acc = fmaf(c.cw[m], raw_in(i - (kMaxConv - 1) + m), acc);
+            ut = silu(acc);
+        } else {
+            ut = raw_to_f32(ch.u[i], tag<TIO>());
+        }
         const float xr = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
         const float dt = step_delta<SOFTPLUS, VAR>(xr, c);
         sdelta += dt;
@@ -432,7 +456,9 @@ __device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const T
 
 template <int N, bool SOFTPLUS, int VAR, typename TIO>
 __device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta, const TIO *Bm,
-                                                 const WaveCtx &c, float (&x)[N], float &sdelta)
+                                                 const WaveCtx &c,
+                                                 const float (&win)[kMaxConv - 1],
+                                                 float (&x)[N], float &sdelta)
 {
     constexpr int TT = TTS;
     const int64_t nchunks = (c.l_end - c.l_begin + TT - 1) / TT;
@@ -444,20 +470,20 @@ __device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta,
     // the last chunk may be partial; every other chunk is full
     load_chunk<false, VAR>(B, u, delta, (const TIO *)nullptr, c, t0 - TT);
     if (t0 + TT <= c.l_end)
-        summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, Bm, c, t0, Q, x, sdelta);
+        summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, B, k > 0, win, Bm, c, t0, Q, x, sdelta);
     else
-        summary_chunk_rev<N, SOFTPLUS, false, VAR>(A, Bm, c, t0, Q, x, sdelta);
+        summary_chunk_rev<N, SOFTPLUS, false, VAR>(A, B, k > 0, win, Bm, c, t0, Q, x, sdelta);
     for (;;) {
         if (--k < 0)
             break;
         t0 -= TT;
         load_chunk<false, VAR>(A, u, delta, (const TIO *)nullptr, c, t0 - TT);
-        summary_chunk_rev<N, SOFTPLUS, true, VAR>(B, Bm, c, t0, Q, x, sdelta);
+        summary_chunk_rev<N, SOFTPLUS, true, VAR>(B, A, k > 0, win, Bm, c, t0, Q, x, sdelta);
         if (--k < 0)
             break;
         t0 -= TT;
         load_chunk<false, VAR>(B, u, delta, (const TIO *)nullptr, c, t0 - TT);
-        summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, Bm, c, t0, Q, x, sdelta);
+        summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, B, k > 0, win, Bm, c, t0, Q, x, sdelta);
     }
 }
 
@@ -654,11 +680,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
     const bool gated = !SUMMARY && z != nullptr;
 #define SELSCAN_RUN(G, SP, PW)                                                                    \
     run_part<N, SUMMARY, G, SP, PW, VAR>(u, delta, z, y, Bm, Cm, c, A2, invA, h, sdelta, win)
-    if (SUMMARY && pow_path && !ZOH && !CONV) {
+    if (SUMMARY && pow_path && !ZOH) {
         if (EXT || delta_softplus)
-            summary_part_rev<N, true, VAR>(u, delta, Bm, c, h, sdelta);
+            summary_part_rev<N, true, VAR>(u, delta, Bm, c, win, h, sdelta);
         else
-            summary_part_rev<N, false, VAR>(u, delta, Bm, c, h, sdelta);
+            summary_part_rev<N, false, VAR>(u, delta, Bm, c, win, h, sdelta);
     } else if (gated) {
         if (EXT || delta_softplus) {
             if (pow_path) SELSCAN_RUN(true, true, true); else SELSCAN_RUN(true, true, false);
