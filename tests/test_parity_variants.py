@@ -188,6 +188,15 @@ def test_reverse_alone_is_default_forward_flipped_bitwise(device, N, dtype, shap
     assert torch.equal(y_r, f(y_f)) and torch.equal(h_r, h_f)
 
 
+@pytest.mark.parametrize("flags,conv", [(ZOH | REV, True), (0, True), (ZOH, False)])
+def test_variants_long_sequence_many_parts(device, flags, conv):
+    """One channel group over a long sequence: thousands of parts, whose entry
+    states go through the two-level carry."""
+    inp = si.make_fwd_inputs(1, 1 << 16, 64, 16, si.F32, True, seed=1250 + flags, h0=True)
+    check_ex(inp, device, flags, si.conv_params(64, 4, 1251) if conv else None,
+             what="long, many parts")
+
+
 @pytest.mark.parametrize("flags", [ZOH | REV, REV])
 def test_variants_layer_workload(device, flags):
     """The 130M-layer shape (batch 8, L 2048, D 1536, N 16, bf16, gate) with
