@@ -12,11 +12,10 @@ namespace selscan {
 // Default (measured on MI355X): waves_per_slot_x2 / 2 waves per wave slot of
 // the chip (1024 SIMDs x the kernel's waves per SIMD) when the channel groups
 // are few; with many groups, at least 8 parts (when L allows), since smaller
-// waves balance the tail of the grid better than fewer, longer ones.  Where
-// each main-pass wave folds the summaries of the parts before it, the fold
-// grows with the part count, so those plans aim at one wave per slot; with
-// carried entry states, 1.5 (mamba130m_layer: 32 parts of 64 steps, 8% faster
-// than 22 parts; long_seq 192 parts).  Parts are whole multiples of kStreamTT
+// waves balance the tail of the grid better than fewer, longer ones: the
+// default forward aims at 1.5 waves per slot (mamba130m_layer: 32 parts of 64
+// steps, 8% faster than 22 parts; long_seq 192 parts), the variants and the
+// backward, at their own occupancies, at one.  Parts are whole multiples of kStreamTT
 // steps and at least 4 of them long.
 StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd,
                             int waves_per_slot_x2)

@@ -188,6 +188,24 @@ def test_reverse_alone_is_default_forward_flipped_bitwise(device, N, dtype, shap
     assert torch.equal(y_r, f(y_f)) and torch.equal(h_r, h_f)
 
 
+@pytest.mark.parametrize("parts", [2, 3, 4])
+def test_few_parts_fold_in_kernel(device, monkeypatch, parts):
+    """Sequences split into at most 4 parts fold the part summaries in the
+    main pass instead of a carry launch; the part count forced through
+    SELSCAN_STREAM_PARTS, default path and variants."""
+    monkeypatch.setenv("SELSCAN_STREAM_PARTS", str(parts))
+    inp = si.make_fwd_inputs(2, 777, 130, 16, si.BF16, True, seed=1260 + parts, h0=True)
+    t = si.fwd_tensors(inp, device)
+    y, hL = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                           t["delta_bias"], True, t["h0"], return_last_state=True)
+    torch.cuda.synchronize()
+    ey, eh = oracle.fwd_inputs(inp)
+    assert rel_err(to_np(y), ey) <= TOL[si.BF16] and rel_err(to_np(hL), eh) <= TOL[si.BF16]
+    for flags, conv in [(0, True), (REV, False), (ZOH | REV, True)]:
+        check_ex(inp, device, flags, si.conv_params(130, 4, 1261) if conv else None,
+                 what="%d parts" % parts)
+
+
 @pytest.mark.parametrize("flags,conv", [(ZOH | REV, True), (0, True), (ZOH, False)])
 def test_variants_long_sequence_many_parts(device, flags, conv):
     """One channel group over a long sequence: thousands of parts, whose entry
