@@ -7,43 +7,89 @@
 namespace selscan {
 namespace bwd {
 
-// out[i] = sum_k in[k * P + i] for i < P, k < K: a block of four waves owns 64
-// columns; wave w adds the rows k = w, w + 4, ... (eight loads in flight),
-// then the four sums are added in wave order.
-__global__ __launch_bounds__(256) void bwd_colsum_kernel(const float *__restrict__ in,
-                                                         float *__restrict__ out, int64_t P,
-                                                         int64_t K)
+// The column sums of all the partials of one backward call in one launch:
+// for each job, out[i] = sum_k in[k * P + i] for i < P, k < K.  A block of 16
+// waves owns 16 / S groups of 64 columns of one job; the S waves of a group
+// add the rows k = s, s + S, ... (eight loads in flight), then their S sums
+// are added in wave order, so the result does not depend on timing.  S grows
+// with K (1, 4 or 16): the long, narrow reductions (dD, dbias over every
+// wave's partial) are split over more waves, the short, wide ones (dB, dC
+// over the channel groups) not at all.  The jobs' blocks follow each other
+// in the grid, so the small, latency-bound jobs run beside the large ones.
+constexpr int kColsumWaves = 16;
+
+__host__ __device__ inline int colsum_split(int64_t K)
 {
-    __shared__ float part[4][kLanes];
-    const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x >> 6;
-    const int64_t i = (int64_t)blockIdx.x * kLanes + lane;
+    return K >= 128 ? 16 : K >= 32 ? 4 : 1;
+}
+
+__global__ __launch_bounds__(kLanes * kColsumWaves) void bwd_colsum_kernel(ColsumJobs jobs)
+{
+    __shared__ float part[kColsumWaves][kLanes];
+    const int lane = threadIdx.x & (kLanes - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // this block's job (fields read at constant offsets: no dynamic indexing
+    // of the argument block)
+    const int64_t blk = blockIdx.x;
+    const float *in = jobs.j[0].in;
+    float *out = jobs.j[0].out;
+    int64_t P = jobs.j[0].P, K = jobs.j[0].K, b0 = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxColsumJobs; ++q) {
+        if (q < jobs.n && blk >= jobs.j[q].block0) {
+            in = jobs.j[q].in;
+            out = jobs.j[q].out;
+            P = jobs.j[q].P;
+            K = jobs.j[q].K;
+            b0 = jobs.j[q].block0;
+        }
+    }
+    const int S = colsum_split(K);
+    const int grp = wave / S, sl = wave % S;
+    const int64_t i = ((blk - b0) * (kColsumWaves / S) + grp) * kLanes + lane;
     float s = 0.0f;
     if (i < P) {
-        int64_t k = wave;
-        for (; k + 28 < K; k += 32) {
+        int64_t k = sl;
+        for (; k + 7 * S < K; k += 8 * S) {
             float v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                v[j] = in[(k + 4 * j) * P + i];
+                v[j] = in[(k + S * j) * P + i];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 s += v[j];
         }
-        for (; k < K; k += 4)
+        for (; k < K; k += S)
             s += in[k * P + i];
     }
     part[wave][lane] = s;
     __syncthreads();
-    if (wave == 0 && i < P)
-        out[i] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    if (sl == 0 && i < P) {
+        float t = part[wave][lane];
+        for (int w = 1; w < S; ++w)
+            t += part[wave + w][lane];
+        out[i] = t;
+    }
 }
 
-hipError_t launch_colsum(const float *in, float *out, int64_t P, int64_t K, hipStream_t s)
+void ColsumJobs::add(const float *in, float *out, int64_t P, int64_t K)
 {
-    if (!out || P <= 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(bwd_colsum_kernel, dim3((unsigned)((P + kLanes - 1) / kLanes)), dim3(256),
-                       0, s, in, out, P, K);
+    ColsumJob &c = j[n++];
+    c.in = in;
+    c.out = out;
+    c.P = P;
+    c.K = K;
+    c.block0 = blocks;
+    const int64_t cols = (int64_t)kLanes * (kColsumWaves / colsum_split(K));
+    blocks += (P + cols - 1) / cols;
+}
+
+hipError_t launch_colsums(const ColsumJobs &jobs, hipStream_t s)
+{
+    if (jobs.n < 1 || jobs.n > kMaxColsumJobs || jobs.blocks > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_colsum_kernel, dim3((unsigned)jobs.blocks),
+                       dim3(kLanes * kColsumWaves), 0, s, jobs);
     return hipGetLastError();
 }
 

@@ -840,7 +840,21 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_conv_fixup_kernel(
 // ---------------------------------------------------------------------------
 // 5. reductions of the partials (fixed order), workspace layout and launch
 // ---------------------------------------------------------------------------
-hipError_t launch_colsum(const float *in, float *out, int64_t P, int64_t K, hipStream_t s);
+// Column sums of the partials (bwd_stream.hip): every reduction of one call
+// in one launch.
+constexpr int kMaxColsumJobs = 7;
+struct ColsumJob {
+    const float *in;
+    float *out;
+    int64_t P, K, block0;
+};
+struct ColsumJobs {
+    ColsumJob j[kMaxColsumJobs] = {};
+    int n = 0;
+    int64_t blocks = 0;
+    void add(const float *in, float *out, int64_t P, int64_t K);
+};
+hipError_t launch_colsums(const ColsumJobs &jobs, hipStream_t s);
 
 struct BwdLayout {
     StreamPlan p;
@@ -943,19 +957,17 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     }
     const int64_t count = a.fwd.batch * a.fwd.L * N;
     const int64_t slots = a.fwd.batch * p.parts;
-    if ((err = launch_colsum(o.pB, a.dB, count, w.gpr, s)) != hipSuccess ||
-        (err = launch_colsum(o.pC, a.dC, count, w.gpr, s)) != hipSuccess ||
-        (err = launch_colsum(o.pA, a.dA, a.fwd.dim * N, slots, s)) != hipSuccess ||
-        (err = launch_colsum(o.pD, a.dD, a.fwd.dim, slots, s)) != hipSuccess ||
-        (err = launch_colsum(o.pbias, a.ddelta_bias, a.fwd.dim, slots, s)) != hipSuccess)
-        return err;
+    ColsumJobs jobs;
+    jobs.add(o.pB, a.dB, count, w.gpr);
+    jobs.add(o.pC, a.dC, count, w.gpr);
+    jobs.add(o.pA, a.dA, a.fwd.dim * N, slots);
+    jobs.add(o.pD, a.dD, a.fwd.dim, slots);
+    jobs.add(o.pbias, a.ddelta_bias, a.fwd.dim, slots);
     if (CONV) {
-        if ((err = launch_colsum(o.pW, a.dconv_w, a.fwd.dim * x.conv_k, slots, s)) !=
-                hipSuccess ||
-            (err = launch_colsum(o.pWb, a.dconv_b, a.fwd.dim, slots, s)) != hipSuccess)
-            return err;
+        jobs.add(o.pW, a.dconv_w, a.fwd.dim * x.conv_k, slots);
+        jobs.add(o.pWb, a.dconv_b, a.fwd.dim, slots);
     }
-    return hipGetLastError();
+    return launch_colsums(jobs, s);
 }
 
 template <int VAR>
