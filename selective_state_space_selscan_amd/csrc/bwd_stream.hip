@@ -74,6 +74,10 @@ __global__ __launch_bounds__(kLanes * kColsumWaves) void bwd_colsum_kernel(Colsu
 
 void ColsumJobs::add(const float *in, float *out, int64_t P, int64_t K)
 {
+    if (n >= kMaxColsumJobs) {
+        n = kMaxColsumJobs + 1;   // the table is full: launch_colsums refuses it
+        return;
+    }
     ColsumJob &c = j[n++];
     c.in = in;
     c.out = out;
