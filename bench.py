@@ -454,8 +454,8 @@ def main():
         parse_pmc(w, *args.parse_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the scan shards over (batch, dim) "
-              "with no exchange, so multi-GPU throughput is not measured here.", file=sys.stderr)
+        print("bench.py: one GPU only: the scan shards over (batch, dim) with no exchange, "
+              "so throughput on several GPUs is not measured.", file=sys.stderr)
         sys.exit(2)
     if w.decode_steps:
         bench_decode(w, args.steps, args.warmup)
