@@ -9,16 +9,18 @@
 namespace selscan {
 
 // SELSCAN_STREAM_PARTS=P overrides the number of sequence parts (tuning knob).
-// Default (measured on MI355X): waves_per_slot_x2 / 2 waves per wave slot of
-// the chip (1024 SIMDs x the kernel's waves per SIMD) when the channel groups
-// are few; with many groups, at least 8 parts (when L allows), since smaller
-// waves balance the tail of the grid better than fewer, longer ones: the
-// default forward aims at 1.5 waves per slot (mamba130m_layer: 32 parts of 64
-// steps, 8% faster than 22 parts; long_seq 192 parts), the variants and the
-// backward, at their own occupancies, at one.  Parts are whole multiples of kStreamTT
-// steps and at least 4 of them long.
+// Default (measured on MI355X with the clocks ramped up): waves_per_slot_x2 / 2
+// waves per wave slot of the chip (1024 SIMDs x the kernel's waves per SIMD)
+// when the channel groups are few; with many groups, at least 8 parts (when L
+// allows), since smaller waves balance the tail of the grid better than fewer,
+// longer ones, and for the same reason on a long sequence parts of at most
+// max_part_len steps.  The default forward: one wave per slot, parts of at
+// most 416 steps: mamba130m_layer 22 parts of 96 steps (1.5 % faster than 32
+// of 64), long_seq 316 parts of 416 (2.7 % faster than 192 of 684),
+// large_layer 8 parts of 256.  Parts are whole multiples of kStreamTT steps
+// and at least 4 of them long.
 StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd,
-                            int waves_per_slot_x2)
+                            int waves_per_slot_x2, int64_t max_part_len)
 {
     constexpr int kLanes = stream::kLanes;
     constexpr int TT = kStreamTT;
@@ -26,7 +28,9 @@ StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per
     p.groups = batch * ((dim + kLanes - 1) / kLanes);
     const int64_t target_waves = 512 * (int64_t)waves_per_simd * waves_per_slot_x2;
     int64_t parts = (target_waves + p.groups - 1) / p.groups;
-    const int64_t min_parts = L / 256 < 8 ? L / 256 : 8;
+    int64_t min_parts = L / 256 < 8 ? L / 256 : 8;
+    if (max_part_len > 0 && (L + max_part_len - 1) / max_part_len > min_parts)
+        min_parts = (L + max_part_len - 1) / max_part_len;
     if (parts < min_parts)
         parts = min_parts;
     const char *e = getenv("SELSCAN_STREAM_PARTS");
@@ -46,11 +50,16 @@ StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per
     return p;
 }
 
+StreamPlan default_fwd_plan(int64_t batch, int64_t L, int64_t dim)
+{
+    return make_stream_plan(batch, L, dim, 4, 2, kDefaultFwdMaxPartLen);
+}
+
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N)
 {
     // the default forward's plan has the most parts (the other plans aim at
     // fewer waves): the part summaries, then the entry states of the parts
-    const StreamPlan p = make_stream_plan(batch, L, dim, 4, kDefaultFwdSlotsX2);
+    const StreamPlan p = default_fwd_plan(batch, L, dim);
     if (p.parts <= 1)
         return 0;
     const size_t summ = (size_t)p.groups * (p.parts - 1) * (N + 1) * stream::kLanes * 4;
@@ -286,7 +295,7 @@ hipError_t launch_default(const FwdArgs &a, const StreamPlan &p, float *summ, fl
 
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream)
 {
-    const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, 4, kDefaultFwdSlotsX2);
+    const StreamPlan p = default_fwd_plan(a.batch, a.L, a.dim);
     float *summ = stream::summary_buffer(a.workspace);
     float *entry = stream::entry_buffer(a.workspace, p, a.N);
     return a.dtype == 1 ? launch_default<uint16_t>(a, p, summ, entry, stream)

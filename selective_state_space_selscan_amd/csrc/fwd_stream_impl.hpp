@@ -818,7 +818,7 @@ hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
             // reverse alone: the default's plan, carry kernel and code with the
             // addressing mirrored (157 -> 134..142 us on batch 8, L 2048,
             // D 1536, N 16, against the run-time direction)
-            const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, 4, kDefaultFwdSlotsX2);
+            const StreamPlan p = default_fwd_plan(a.batch, a.L, a.dim);
             float *entry = entry_buffer(a.workspace, p, N);
             ExtParams none{};
             return bf ? launch_n<N, kVarRev, uint16_t>(a, none, p, summ, entry, s)

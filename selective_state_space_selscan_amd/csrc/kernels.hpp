@@ -59,11 +59,15 @@ struct StreamPlan {
     int parts;
 };
 // waves_per_simd: the kernel's occupancy; the plan aims at waves_per_slot_x2 / 2
-// waves per wave slot of the chip (3: the default forward, whose main pass
-// reads carried entry states; 2: plans whose main pass folds the summaries).
+// waves per wave slot of the chip; max_part_len (0: none) caps the length of a
+// part.
 StreamPlan make_stream_plan(int64_t batch, int64_t L, int64_t dim, int waves_per_simd = 4,
-                            int waves_per_slot_x2 = 2);
-constexpr int kDefaultFwdSlotsX2 = 3;
+                            int waves_per_slot_x2 = 2, int64_t max_part_len = 0);
+// The plan of the default forward (and of the reverse-alone variant, which
+// runs the same code): one wave per slot at four waves per SIMD, parts of at
+// most kDefaultFwdMaxPartLen steps.
+constexpr int64_t kDefaultFwdMaxPartLen = 416;
+StreamPlan default_fwd_plan(int64_t batch, int64_t L, int64_t dim);
 size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
 
