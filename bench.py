@@ -6,6 +6,7 @@
     python bench.py --pass bwd           # the backward (selscan_bwd) on the same workload
     python bench.py --variant zoh,rev,conv4   # forward variants through selscan_fwd_ex
     python bench.py --pass bwd --variant zoh,rev,conv4   # their backward (selscan_bwd_ex)
+    python bench.py --pass fwdbwd        # forward + backward reusing its part state
 
 One step = one selscan_fwd call over one batch of the workload.  The default
 workload is one Mamba-130M layer: batch 8, L 2048, D 1536, N 16, bf16 inputs,
@@ -356,7 +357,10 @@ def bwd_valu_slots(N, gate, es):
 
 def bench_bwd(w, args):
     """``steps`` selscan_bwd calls on the workload (upstream gradient dy
-    seeded, no dh_last), inputs resident in HBM, one workspace."""
+    seeded, no dh_last), inputs resident in HBM, one workspace.  With
+    ``--pass fwdbwd`` a step is a training step's pair instead: selscan_fwd
+    into the workspace, then selscan_bwd_ex reading the forward's part state
+    from it (SELSCAN_FLAG_REUSE_FWD_STATE; plain or reverse alone)."""
     import torch
 
     import selscan_inputs as si
@@ -376,8 +380,21 @@ def bench_bwd(w, args):
     if vconv:
         cw, cb = si.conv_params(w.dim, vconv, w.seed)
         conv_w, conv_b = torch.from_numpy(cw).to(dev), torch.from_numpy(cb).to(dev)
+    pair = args.which == "fwdbwd"
+    if pair and (vconv or vflags & ~ss.SELSCAN_FLAG_REVERSE):
+        raise SystemExit("bench.py: --pass fwdbwd runs the plain path or 'rev' alone")
+    y = torch.empty_like(t["u"])
 
     def step(i):
+        if pair:
+            ss.selscan_fwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                              t["delta_bias"], True, None, flags=vflags, y=y, workspace=ws,
+                              stream=stream)
+            ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"],
+                              t["z"], t["delta_bias"], True, None, None,
+                              flags=vflags | ss.SELSCAN_FLAG_REUSE_FWD_STATE, workspace=ws,
+                              stream=stream)
+            return
         if args.variant:
             ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"],
                               t["z"], t["delta_bias"], True, None, None, flags=vflags,
@@ -389,32 +406,40 @@ def bench_bwd(w, args):
     wall, call_mean, call_ms = timed_steps(step, args.steps, args.warmup, stream)
     es = 2 if w.dtype == si.BF16 else 4
     elems = w.batch * w.L * w.dim
-    slots = bwd_valu_slots(w.N, w.gate, es) * elems
+    slots_el = bwd_valu_slots(w.N, w.gate, es) + (algorithmic_valu_slots(w.N, w.gate, es)
+                                                   if pair else 0)
+    slots = slots_el * elems
     # bytes the backward must move: the forward's inputs once, dy, and the
     # gradients du, ddelta, dz (dtype) and dB, dC (fp32) once
     nb = (elems * ((3 if w.gate else 2) * es + es + (3 if w.gate else 2) * es)
           + 2 * w.batch * w.L * w.N * (es + 4) + w.dim * w.N * 8 + 4 * w.dim * 4)
+    if pair:
+        nb += algorithmic_bytes(w.batch, w.L, w.dim, w.N, es, w.gate)
     achieved = slots / (call_mean * 1e-3) / 1e9
     res = {
-        "metric": "selective-scan bwd elements(B*L*D)/s, 1 GPU",
+        "metric": "selective-scan %s elements(B*L*D)/s, 1 GPU" % ("fwd+bwd" if pair else "bwd"),
         "value": elems / (wall / args.steps), "unit": "elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * wall / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == si.BF16 else "f32", "data": "synthetic (seeded)",
-        "config": {"workload": w.name, "pass": "bwd", "batch": w.batch, "L": w.L, "dim": w.dim,
+        "config": {"workload": w.name, "pass": args.which, "batch": w.batch, "L": w.L,
+                   "dim": w.dim,
                    "N": w.N, "gate": w.gate},
         "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms))},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_SLOTS / 1e9,
                      "unit": "G VALU lane-slots/s", "frac": achieved * 1e9 / VALU_PEAK_SLOTS,
-                     "traffic": None, "kernel": "selscan_bwd call (all passes)",
-                     "algorithmic_slots_per_element": bwd_valu_slots(w.N, w.gate, es),
+                     "traffic": None,
+                     "kernel": ("selscan_fwd + selscan_bwd_ex (reusing the forward's part "
+                                "state)" if pair else "selscan_bwd call (all passes)"),
+                     "algorithmic_slots_per_element": slots_el,
                      "algorithmic_bytes_per_call": nb,
                      "hbm_gbps_of_call": nb / (call_mean * 1e-3) / 1e9},
     }
     if args.variant:
         res["variant"] = args.variant
-        res["roofline"]["kernel"] = "selscan_bwd_ex call (%s); slots of the default path" \
-            % args.variant
+        if not pair:
+            res["roofline"]["kernel"] = "selscan_bwd_ex call (%s); slots of the default path" \
+                % args.variant
     print(json.dumps(res), flush=True)
 
 
@@ -444,7 +469,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fwdbwd"), default="fwd")
     ap.add_argument("--variant", default="", help="variants: zoh, rev, convK (fwd or bwd)")
     args = ap.parse_args()
 
@@ -463,7 +488,7 @@ def main():
     if args.pmc_run:
         pmc_run(w)
         return
-    if args.which == "bwd":
+    if args.which in ("bwd", "fwdbwd"):
         bench_bwd(w, args)
         return
     vflags, vconv = parse_variant(args.variant)

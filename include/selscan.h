@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 4
+#define SELSCAN_ABI_VERSION 5
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -161,6 +161,7 @@ int selscan_fwd(const void *u, const void *delta, const float *A,
 /* Flags of selscan_fwd_ex. */
 #define SELSCAN_FLAG_ZOH_EXACT 1   /* B_bar = (exp(Delta A) - 1) / A * B, Delta B where A = 0 */
 #define SELSCAN_FLAG_REVERSE   2   /* scan from t = L-1 down to t = 0                      */
+#define SELSCAN_FLAG_REUSE_FWD_STATE 4   /* selscan_bwd_ex only: see there                 */
 #define SELSCAN_MAX_CONV_WIDTH 4
 
 /*
@@ -276,6 +277,17 @@ int selscan_bwd(const void *u, const void *delta, const float *A,
  * sums in a fixed order (bitwise repeatable) like dA.  Errors as selscan_bwd
  * and selscan_fwd_ex, and SELSCAN_ERR_NULL for conv_width > 0 without
  * dconv_weight.
+ *
+ * SELSCAN_FLAG_REUSE_FWD_STATE (in flags, with REVERSE or alone; not with
+ * ZOH_EXACT or conv_width > 0, SELSCAN_ERR_UNSUPPORTED): the workspace is the
+ * one the matching forward last ran in (selscan_fwd, or selscan_fwd_ex with
+ * the same REVERSE flag and no other variant) with the same u, delta, A, Bm,
+ * delta_bias, delta_softplus, h0 and sizes, and still holds that forward's
+ * sequence-part summaries and part entry states, which the backward then
+ * reads instead of recomputing (the forward's summary and carry passes).
+ * The result is bit for bit that of the call without the flag.  The library
+ * cannot check the correspondence: it is the caller's to keep.  A workspace
+ * of selscan_bwd_workspace_bytes is large enough for the forward too.
  */
 int selscan_bwd_ex(const void *u, const void *delta, const float *A,
                    const void *Bm, const void *Cm, const float *D_skip,

@@ -17,6 +17,7 @@ is no CPU fallback.  If ``libselscan.so`` is missing, every call raises.
 from ._abi import (  # noqa: F401
     SELSCAN_BF16,
     SELSCAN_F32,
+    SELSCAN_FLAG_REUSE_FWD_STATE,
     SELSCAN_FLAG_REVERSE,
     SELSCAN_FLAG_ZOH_EXACT,
     SELSCAN_MAX_CONV_WIDTH,

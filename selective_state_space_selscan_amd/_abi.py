@@ -16,6 +16,7 @@ SELSCAN_F32 = 0
 SELSCAN_BF16 = 1
 SELSCAN_FLAG_ZOH_EXACT = 1
 SELSCAN_FLAG_REVERSE = 2
+SELSCAN_FLAG_REUSE_FWD_STATE = 4
 SELSCAN_MAX_CONV_WIDTH = 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -240,7 +241,14 @@ def selscan_bwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: to
     """Gradients of ``selscan_fwd_ex`` (same ``flags``, ``conv_weight``,
     ``conv_bias``) through ``selscan_bwd_ex``.  The dict of ``selscan_bwd``,
     plus dconv_weight (dim, k) and dconv_bias (dim,) in float32 with the conv
-    prologue (None without); du is then the gradient of the conv's input u."""
+    prologue (None without); du is then the gradient of the conv's input u.
+
+    With SELSCAN_FLAG_REUSE_FWD_STATE in ``flags`` (plain or REVERSE alone),
+    ``workspace`` must be the tensor the matching forward (``selscan_fwd``,
+    or ``selscan_fwd_ex`` with the same REVERSE flag) last ran in, on the
+    same inputs, h0 and sizes, at least ``selscan_bwd_workspace_bytes``
+    long; the backward then reads that forward's part summaries and entry
+    states instead of recomputing them (same result, bit for bit)."""
     return _bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, delta_softplus, h0, dh_last,
                 workspace, stream, (int(flags), conv_weight, conv_bias))
 
@@ -275,7 +283,12 @@ def _bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, delta_softplus, h0, dh_
              ddelta_bias=torch.empty((dim,), dtype=f32, device=dev),
              dh0=torch.empty((batch, dim, N), dtype=f32, device=dev))
     ws_bytes = int(L_.selscan_bwd_workspace_bytes(batch, L, dim, N, code))
-    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+    if ex is not None and ex[0] & SELSCAN_FLAG_REUSE_FWD_STATE:
+        # the forward's part state is in the caller's workspace: never replace it
+        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError("SELSCAN_FLAG_REUSE_FWD_STATE needs the forward's workspace, "
+                             "at least selscan_bwd_workspace_bytes (%d) long" % ws_bytes)
+    elif workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     common = (_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z),
               _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dh_last),

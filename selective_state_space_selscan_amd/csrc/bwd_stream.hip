@@ -115,9 +115,12 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N)
     const size_t slots = (size_t)batch * w.p.parts;
     size_t off = 0;
     const size_t entry = (size_t)w.p.groups * w.p.parts * N * kLanes * 4;
+    // the forward's part summaries and entry states first, at the offsets
+    // the default forward uses (summary_buffer, entry_buffer): a backward with
+    // SELSCAN_FLAG_REUSE_FWD_STATE reads them where the forward left them
     w.fsumm = off; off = align256(off + summ);
-    w.asumm = off; off = align256(off + summ);
     w.fentry = off; off = align256(off + entry);
+    w.asumm = off; off = align256(off + summ);
     w.aentry = off; off = align256(off + entry);
     w.carry = off; off = align256(off + carry_scratch_bytes(w.p.groups, w.p.parts, N));
     w.ckpt = off; off = align256(off + (size_t)w.p.groups * w.nck * N * kLanes * 4);

@@ -892,7 +892,12 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     hipError_t err;
     const bool split = p.parts > 1;
     float *cscr = (float *)(base + w.carry);   // shared: the two carries run in turn
-    if (split) {
+    // With the forward's part state reused, its summaries are in place, and
+    // its entry states too unless it folded the summaries in its main pass
+    // (a few parts: no carry launch, no entry states written).
+    const bool reuse = (e.flags & kBwdFlagReuseFwdState) != 0;
+    const bool have_fentry = reuse && p.parts > stream::kFoldInKernelMaxParts;
+    if (split && !reuse) {
         err = plain ? launch_fwd_summaries(a.fwd, p, fsumm, s)
                     : launch_fwd_summaries_ext(a.fwd, e, p, fsumm, s);
         if (err != hipSuccess)
@@ -910,9 +915,10 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     };
     // entry states of the parts: from the left (h0) and from the right (dh_last)
     auto carry_fwd = [&]() {
-        return split ? launch_fwd_carry(fsumm, a.fwd.h0, a.fwd.A, fentry, a.fwd.batch, a.fwd.dim,
-                                        N, p.parts, 0, cscr, s)
-                     : hipSuccess;
+        return split && !have_fentry
+                   ? launch_fwd_carry(fsumm, a.fwd.h0, a.fwd.A, fentry, a.fwd.batch, a.fwd.dim,
+                                      N, p.parts, 0, cscr, s)
+                   : hipSuccess;
     };
     auto carry_adj = [&]() {
         return split ? launch_fwd_carry(asumm, a.dh_last, a.fwd.A, aentry, a.fwd.batch,

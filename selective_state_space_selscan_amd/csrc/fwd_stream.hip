@@ -366,6 +366,9 @@ hipError_t launch_fwd_summaries_ext(const FwdArgs &a, const FwdExt &e, const Str
 
 hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream)
 {
+    // no variant: the default forward itself (same plan, same bits)
+    if (e.flags == 0 && e.conv_k == 0)
+        return launch_fwd_stream(a, stream);
     const bool zoh = (e.flags & kFwdFlagZohExact) != 0;
 #define SELSCAN_EXT_CASE(NN)                                                                      \
     case NN:                                                                                      \

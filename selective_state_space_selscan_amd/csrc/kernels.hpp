@@ -78,6 +78,7 @@ hipError_t launch_fwd_lookback(const FwdArgs &a, hipStream_t stream);
 // Variants of the streaming forward (same plan and workspace).
 constexpr int kFwdFlagZohExact = 1;
 constexpr int kFwdFlagReverse = 2;
+constexpr int kBwdFlagReuseFwdState = 4;   // backward: the workspace holds the forward's part state
 struct FwdExt {
     int flags;            // kFwdFlagZohExact | kFwdFlagReverse
     const float *conv_w;  // (dim, conv_k) when conv_k > 0

@@ -335,15 +335,21 @@ int selscan_bwd_ex(const void *u, const void *delta, const float *A, const void 
                    float *dconv_bias, int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
                    void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE))
+    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_REUSE_FWD_STATE))
         return SELSCAN_ERR_UNSUPPORTED;
     if (conv_width < 0)
         return SELSCAN_ERR_SHAPE;
     if (conv_width > SELSCAN_MAX_CONV_WIDTH)
         return SELSCAN_ERR_UNSUPPORTED;
+    // the forward's part state has the backward's layout only where both run
+    // the default plan: the plain forward and the reverse-alone variant
+    if ((flags & SELSCAN_FLAG_REUSE_FWD_STATE) &&
+        ((flags & SELSCAN_FLAG_ZOH_EXACT) || conv_width > 0))
+        return SELSCAN_ERR_UNSUPPORTED;
     selscan::FwdExt e;
     e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |
-              (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0);
+              (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0) |
+              (flags & SELSCAN_FLAG_REUSE_FWD_STATE ? selscan::kBwdFlagReuseFwdState : 0);
     e.conv_w = conv_weight;
     e.conv_b = conv_bias;
     e.conv_k = (int)conv_width;

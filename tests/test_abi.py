@@ -238,6 +238,10 @@ def bwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, dconv_w=None, d
 
 INVALID_BWD_EX = [
     ("unknown_flag", dict(flags=8), ERR_UNSUP),
+    # the forward's part state is reusable only where both run the default plan
+    ("reuse_with_zoh", dict(flags=4 | 1), ERR_UNSUP),
+    ("reuse_with_conv", dict(flags=4, conv_width=4, conv_w=fake(22), dconv_w=fake(24)),
+     ERR_UNSUP),
     ("conv_width_5", dict(conv_width=5, conv_w=fake(22), dconv_w=fake(24)), ERR_UNSUP),
     ("conv_width_neg", dict(conv_width=-2, conv_w=fake(22), dconv_w=fake(24)), ERR_SHAPE),
     ("conv_w_null", dict(conv_width=4, dconv_w=fake(24)), ERR_NULL),
@@ -267,6 +271,12 @@ def test_bwd_ex_rejects_invalid_arguments(name, kw, status):
     L = ss.lib()
     assert L.selscan_bwd_ex(*bwd_ex_args(**kw)) == status
     assert L.selscan_last_hip_error() == 0
+
+
+def test_flag_constants_match_header():
+    assert ss.SELSCAN_FLAG_ZOH_EXACT == header_constant("SELSCAN_FLAG_ZOH_EXACT")
+    assert ss.SELSCAN_FLAG_REVERSE == header_constant("SELSCAN_FLAG_REVERSE")
+    assert ss.SELSCAN_FLAG_REUSE_FWD_STATE == header_constant("SELSCAN_FLAG_REUSE_FWD_STATE")
 
 
 def test_workspace_size_zero_when_grids_do_not_fit():
