@@ -187,6 +187,9 @@ int selscan_fwd(const void *u, const void *delta, const float *A,
  *                                   u[b, t-(conv_width-1)+j, d])
  *                with u = 0 before t = 0, and D u in the readout uses u'.
  *
+ * With flags = 0 and conv_width = 0 this is the default forward itself (the
+ * results of selscan_fwd bit for bit).
+ *
  * Workspace: the same size as selscan_fwd (selscan_fwd_workspace_bytes).
  * Errors as selscan_fwd, and: SELSCAN_ERR_UNSUPPORTED for an unknown flag bit
  * or conv_width > SELSCAN_MAX_CONV_WIDTH, SELSCAN_ERR_SHAPE for conv_width < 0,
