@@ -333,10 +333,11 @@ __device__ __forceinline__ void checkpoint_part(const TIO *__restrict__ u,
 // Passes 2 and 3 in one launch (ROLES = 3): the adjoint summaries
 // (arithmetic-bound) and the checkpoints (bound by their stores) are
 // independent, and sharing the CUs lets one's arithmetic overlap the other's
-// memory traffic: 3.6 % off the plain backward, measured.  Blocks alternate
-// between the roles while both have work left.  ROLES = 1 or 2: one role
-// alone (the variants, whose heavier checkpoint walk would set the occupancy
-// of both roles: 1.5 % slower merged).
+// memory traffic: 3.6 % off the plain backward and 2 % off the conv4 one,
+// measured.  Blocks alternate between the roles while both have work left.
+// ROLES = 1 or 2: one role alone (the exact-ZOH variants, whose heavier
+// checkpoint walk sets the registers of both roles: 0.6 % slower merged with
+// reverse and conv4, no gain without).
 template <int N, int VAR, int ROLES, typename TIO>
 __global__ __launch_bounds__(kLanes * 4) void bwd_pass23_kernel(
     const TIO *__restrict__ u, const TIO *__restrict__ delta, const TIO *__restrict__ z,
@@ -925,7 +926,7 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
                                         a.fwd.dim, N, p.parts, 1, cscr, s)
                      : hipSuccess;
     };
-    if constexpr ((VAR & ~kVarRev) == 0) {
+    if constexpr ((VAR & kVarZoh) == 0) {
         // the checkpoints need the forward entry states
         if ((err = carry_fwd()) != hipSuccess)
             return err;
