@@ -392,8 +392,8 @@ __device__ __forceinline__ void run_part(const TIO *u, const TIO *delta, const T
 // The end state from zero is x[n] = sum_t Q_t^(n+1) Delta_t u_t B_t[n], with
 // Q_t = prod_{s>t} r_s and r_s = exp(Delta_s A[d,0]).  Walking backwards, Q
 // is one running product and Delta_t u_t Q_t^(n+1) one multiply per n, so a
-// (t, n) costs a multiply and an FMA (the forward walk needs three ops).
-// Not used with exact ZOH (its input of a step is not Delta_t u_t).  With the
+// (t, n) costs a multiply and an FMA (the forward walk needs three ops);
+// with exact ZOH three operations (the forward walk: six).  With the
 // conv prologue the input of step i needs the raw inputs of steps i-3..i:
 // inside the chunk, or for its first steps the last raw inputs of the chunk
 // before it (prev: the next chunk of the walk, prefetched while this one
@@ -441,14 +441,33 @@ __device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const C
         const float xr = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
         const float dt = step_delta<SOFTPLUS, VAR>(xr, c);
         sdelta += dt;
-        float g = dt * ut * Q;
+        const float r = hw_exp2(dt * c.A2_0);
+        if constexpr ((VAR & kVarZoh) != 0) {
+            // Exact ZOH: the step adds Q^(n+1) g S_n / (n+1) B_t[n], with
+            // g = (r - 1) / A[d,0] * u and S_n = 1 + r + ... + r^n.  P_n =
+            // Q^(n+1) S_n g follows P_n = Q P_(n-1) + T_n, T_n = Q^(n+1) r^n g =
+            // T_(n-1) Q r; the 1/(n+1) is applied once at the end of the part
+            // (summary_part_rev): three operations per (t, n).
+            const float qr = Q * r;
+            float T = zoh_coeff(dt, dt * c.A2_0, r, c.invA0) * ut * Q;
+            float P = T;
+            x[0] = fmaf(P, row_val<N>(bcur, 0), x[0]);
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            if (n)
-                g *= Q;
-            x[n] = fmaf(g, row_val<N>(bcur, n), x[n]);
+            for (int n = 1; n < N; ++n) {
+                T *= qr;
+                P = fmaf(Q, P, T);
+                x[n] = fmaf(P, row_val<N>(bcur, n), x[n]);
+            }
+        } else {
+            float g = dt * ut * Q;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                if (n)
+                    g *= Q;
+                x[n] = fmaf(g, row_val<N>(bcur, n), x[n]);
+            }
         }
-        Q *= hw_exp2(dt * c.A2_0);
+        Q *= r;
         if (i > 0)
             bcur = bnxt;
     }
@@ -484,6 +503,11 @@ __device__ __forceinline__ void summary_part_rev(const TIO *u, const TIO *delta,
         t0 -= TT;
         load_chunk<false, VAR>(B, u, delta, (const TIO *)nullptr, c, t0 - TT);
         summary_chunk_rev<N, SOFTPLUS, true, VAR>(A, B, k > 0, win, Bm, c, t0, Q, x, sdelta);
+    }
+    if constexpr ((VAR & kVarZoh) != 0) {
+#pragma unroll
+        for (int n = 1; n < N; ++n)
+            x[n] *= 1.0f / (float)(n + 1);
     }
 }
 
@@ -683,7 +707,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
     const bool gated = !SUMMARY && z != nullptr;
 #define SELSCAN_RUN(G, SP, PW)                                                                    \
     run_part<N, SUMMARY, G, SP, PW, VAR>(u, delta, z, y, Bm, Cm, c, A2, invA, h, sdelta, win)
-    if (SUMMARY && pow_path && !ZOH) {
+    if (SUMMARY && pow_path) {
         if (EXT || delta_softplus)
             summary_part_rev<N, true, VAR>(u, delta, Bm, c, win, h, sdelta);
         else
