@@ -857,6 +857,17 @@ hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
     x.conv_b = e.conv_k > 0 ? e.conv_b : nullptr;
     x.conv_k = e.conv_k;
     x.rev = (e.flags & kFwdFlagReverse) ? 1 : 0;
+    if (!x.rev) {
+        // forward direction: the direction and the softplus switch fixed at
+        // compile time
+        constexpr int VF = ZOH ? kVarZoh : 0;
+        if (e.conv_k > 0)
+            return bf ? launch_n<N, VF | kVarConv, uint16_t>(a, x, p, summ, entry, s)
+                      : launch_n<N, VF | kVarConv, float>(a, x, p, summ, entry, s);
+        if constexpr (ZOH)
+            return bf ? launch_n<N, VF, uint16_t>(a, x, p, summ, entry, s)
+                      : launch_n<N, VF, float>(a, x, p, summ, entry, s);
+    }
     constexpr int V = kVarExt | (ZOH ? kVarZoh : 0);
     if (e.conv_k > 0)
         return bf ? launch_n<N, V | kVarConv, uint16_t>(a, x, p, summ, entry, s)
