@@ -1,10 +1,20 @@
 // Variant instantiations of the streaming forward for state size N = 64 with
-// B_bar = Delta B: reverse direction (run-time flag) and the conv1d + SiLU
-// prologue.  One translation unit per (N, B_bar form) so that they compile in
-// parallel.
+// B_bar = Delta B: the variants with REVERSE (the direction a run-time
+// flag), reverse alone, and the summary pass the variants' backward uses; the
+// forward-direction variants are in the matching _fixed unit.  One
+// translation unit per (N, B_bar form) so that they compile in parallel.
 #include "fwd_stream_impl.hpp"
 
 namespace selscan {
+namespace stream {
+// compiled in fwd_stream_ext_n64_fixed.hip
+extern template hipError_t launch_ext_fixed<64, false, uint16_t>(const FwdArgs &, const ExtParams &,
+                                                            const StreamPlan &, float *, float *,
+                                                            hipStream_t);
+extern template hipError_t launch_ext_fixed<64, false, float>(const FwdArgs &, const ExtParams &,
+                                                         const StreamPlan &, float *, float *,
+                                                         hipStream_t);
+} // namespace stream
 
 hipError_t launch_fwd_stream_ext_n64(const FwdArgs &a, const FwdExt &e, hipStream_t stream)
 {

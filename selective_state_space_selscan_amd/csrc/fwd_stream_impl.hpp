@@ -831,6 +831,23 @@ hipError_t launch_ext_summaries(const FwdArgs &a, const FwdExt &e, const StreamP
 
 // Variant forward for one N and one B_bar form (ZOH: exact zero-order hold):
 // picks the instantiation from the conv width and the dtype.
+// The variants in the forward direction, with the direction and the
+// softplus switch fixed at compile time (conv, ZOH, ZOH + conv; the plain
+// case is the default forward).  Instantiated explicitly in the
+// fwd_stream_ext_n*_fixed.hip units, so that they compile in parallel with
+// the run-time-direction ones.
+template <int N, bool ZOH, typename TIO>
+hipError_t launch_ext_fixed(const FwdArgs &a, const ExtParams &x, const StreamPlan &p,
+                            float *summ, float *entry, hipStream_t s)
+{
+    constexpr int VF = ZOH ? kVarZoh : 0;
+    if (x.conv_k > 0)
+        return launch_n<N, VF | kVarConv, TIO>(a, x, p, summ, entry, s);
+    if constexpr (ZOH)
+        return launch_n<N, VF, TIO>(a, x, p, summ, entry, s);
+    return hipErrorInvalidValue;   // no variant: selscan_fwd_ex runs the default forward
+}
+
 template <int N, bool ZOH>
 hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
 {
@@ -857,17 +874,9 @@ hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
     x.conv_b = e.conv_k > 0 ? e.conv_b : nullptr;
     x.conv_k = e.conv_k;
     x.rev = (e.flags & kFwdFlagReverse) ? 1 : 0;
-    if (!x.rev) {
-        // forward direction: the direction and the softplus switch fixed at
-        // compile time
-        constexpr int VF = ZOH ? kVarZoh : 0;
-        if (e.conv_k > 0)
-            return bf ? launch_n<N, VF | kVarConv, uint16_t>(a, x, p, summ, entry, s)
-                      : launch_n<N, VF | kVarConv, float>(a, x, p, summ, entry, s);
-        if constexpr (ZOH)
-            return bf ? launch_n<N, VF, uint16_t>(a, x, p, summ, entry, s)
-                      : launch_n<N, VF, float>(a, x, p, summ, entry, s);
-    }
+    if (!x.rev)
+        return bf ? launch_ext_fixed<N, ZOH, uint16_t>(a, x, p, summ, entry, s)
+                  : launch_ext_fixed<N, ZOH, float>(a, x, p, summ, entry, s);
     constexpr int V = kVarExt | (ZOH ? kVarZoh : 0);
     if (e.conv_k > 0)
         return bf ? launch_n<N, V | kVarConv, uint16_t>(a, x, p, summ, entry, s)
