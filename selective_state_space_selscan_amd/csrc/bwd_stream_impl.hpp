@@ -710,13 +710,14 @@ __device__ __forceinline__ void bwd_part(const TIO *u, const TIO *delta, const T
     }
 }
 
-// Main-pass occupancy: two waves per SIMD (256 VGPRs) up to N = 32; one
-// (512 VGPRs) for N = 64 and for the variants from N = 16 on, whose extra
-// per-state terms would spill at 256.
+// Main-pass occupancy: two waves per SIMD (256 VGPRs) up to N = 16; one
+// (512 VGPRs, spills to AGPRs) from N = 32 on, where two waves spill 474
+// VGPRs to scratch (batch 8, L 2048, D 1536, N 32: 4.35 -> 1.74 ms), and for
+// the variants from N = 16 on, whose extra per-state terms would spill at 256.
 template <int N, int VAR>
 constexpr int bwd_waves_per_eu()
 {
-    if (N > 32)
+    if (N > 16)
         return 1;
     if ((VAR & (kVarZoh | kVarConv)) != 0 && N >= 16)
         return 1;
