@@ -613,12 +613,16 @@ __device__ __forceinline__ void fold_summaries(float (&h)[N], const float *sbase
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for N <= 16;
 // three (at most 168 VGPRs) for the exact-ZOH variants, whose per-state
 // coefficients would spill at 128.  (The conv variant spills a few registers
-// at four waves and is still faster there than at three: measured.)
+// at four waves and is still faster there than at three: measured.)  N = 32:
+// two waves (256 VGPRs, a few spilled: batch 8, L 2048, D 1536 433 -> 274 us
+// against one wave), one for exact ZOH; N = 64: one.
 template <int N, int VAR>
 constexpr int waves_per_eu()
 {
-    if (N > 16)
+    if (N > 32 || (N > 16 && (VAR & kVarZoh) != 0))
         return 1;
+    if (N > 16)
+        return 2;
     return (VAR & kVarZoh) != 0 ? 3 : 4;
 }
 
