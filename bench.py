@@ -69,22 +69,25 @@ def algorithmic_bytes(batch, L, dim, N, es, gate, with_last=False, with_h0=False
     return b
 
 
-def algorithmic_valu_slots(N, gate, es):
+def algorithmic_valu_slots(N, gate, es, general_a=False):
     """fp32 VALU issue slots one (b, l, d) element needs on gfx950 without
-    packed instructions, for A of the S4D-real form (A[d,n] = (n+1) A[d,0]) as
-    in every workload here.  A transcendental (exp2, log2, rcp) takes two
-    slots.
+    packed instructions.  A transcendental (exp2, log2, rcp) takes two slots.
+    For A of the S4D-real form (A[d,n] = (n+1) A[d,0], every workload here):
       per state n: A_bar by one multiply (power chain), Delta*u*B (1), state
                    FMA (1), readout FMA (1)                        -> 4 N
       per element: widen u, Delta (2 if bf16), bias add (1), softplus (exp,
                    log: 4 slots, + 2), Delta*u (1), r = exp(Delta A0) (3),
                    D*u (1), round y (1 if bf16)
       gate:        widen z (1 if bf16), SiLU (exp, rcp: 4 slots, + 2), y*g (1)
-    """
+    For a general A (general_a), A_bar = exp2(Delta A[d,n] log2 e) per state:
+    a multiply and an exp2 (3 slots) in place of the power chain's multiply,
+    and no r: 6 N + the per-element work less 3."""
     bf = 1 if es == 2 else 0
     per = 4 * N + 2 * bf + 1 + 6 + 1 + 3 + 1 + bf
     if gate:
         per += bf + 6 + 1
+    if general_a:
+        per += 2 * N - 3
     return per
 
 
@@ -115,6 +118,18 @@ def load_traffic(workload):
     return t.get("bytes_per_call")
 
 
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp_full, cpu_budget_s=15.0):
     """The oracle (untuned, OpenMP over (b, d)) on the workload, repeated whole
     until about ``cpu_budget_s`` seconds of CPU time (all threads) are spent."""
@@ -131,7 +146,7 @@ def cpu_baseline(w, inp_full, cpu_budget_s=15.0):
     wall = time.perf_counter() - t0
     cpu = time.process_time() - c0
     return {"value": passes * elems_per_pass / wall, "unit": "elements/s", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "%d full pass(es) of %s (%d elements each), %.1f s wall, %.1f s CPU, "
                       "fp64 sequential recurrence, OpenMP over (b, d)"
                       % (passes, w.name, elems_per_pass, wall, cpu)}
@@ -290,27 +305,32 @@ def bench_decode(w, steps, warmup):
 
 def timed_steps(step, steps, warmup, stream, percall=50):
     """``warmup`` untimed steps, then exactly ``steps`` steps back to back,
-    bracketed by a synchronize on both sides (host clock) and by one pair of
-    HIP events on the launch stream (device clock): the average call
-    duration is the event interval / ``steps``.  Then ``percall`` further
-    steps, each between its own pair of events, for the spread of single
-    calls; they are not part of the timed region (an event pair per call
-    adds a small bubble of its own).  Returns (wall s, mean call ms,
-    per-call ms array)."""
+    bracketed by a synchronize on both sides (host clock) and by HIP events on
+    the launch stream (device clock): the average call duration is the
+    interval from the first event to the last / ``steps``.  Events also mark
+    the quarters of the timed steps (when there are at least 4), so the mean
+    call of each quarter shows whether the clocks were still ramping.  Then
+    ``percall`` further steps, each between its own pair of events, for the
+    spread of single calls; they are not part of the timed region (an event
+    pair per call adds a small bubble of its own).  Returns (wall s, mean
+    call ms, per-call ms array, mean call ms per quarter)."""
     import torch
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = sorted({0, steps} | ({steps * q // 4 for q in range(1, 4)} if steps >= 4 else set()))
+    ev = {m: torch.cuda.Event(enable_timing=True) for m in marks}
     t0 = time.perf_counter()
-    a.record(stream)
+    ev[0].record(stream)
     for i in range(steps):
         step(warmup + i)
-    b.record(stream)
+        if i + 1 in ev:
+            ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_mean = a.elapsed_time(b) / steps
+    call_mean = ev[0].elapsed_time(ev[steps]) / steps
+    quarters = [ev[m0].elapsed_time(ev[m1]) / (m1 - m0) for m0, m1 in zip(marks, marks[1:])]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(percall)]
     for i, (x, y) in enumerate(ev):
@@ -318,7 +338,7 @@ def timed_steps(step, steps, warmup, stream, percall=50):
         step(warmup + steps + i)
         y.record(stream)
     torch.cuda.synchronize()
-    return wall, call_mean, np.array([x.elapsed_time(y) for x, y in ev])
+    return wall, call_mean, np.array([x.elapsed_time(y) for x, y in ev]), quarters
 
 
 def device_copy_gbps(dev, nbytes=1 << 29, reps=10):
@@ -332,7 +352,7 @@ def device_copy_gbps(dev, nbytes=1 << 29, reps=10):
     for _ in range(3):
         dst.copy_(src)
     ms = []
-    for _ in range(reps):
+    while len(ms) < reps:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         dst.copy_(src)
@@ -403,7 +423,7 @@ def bench_bwd(w, args):
         ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"], t["z"],
                        t["delta_bias"], True, None, None, workspace=ws, stream=stream)
 
-    wall, call_mean, call_ms = timed_steps(step, args.steps, args.warmup, stream)
+    wall, call_mean, call_ms, quarters = timed_steps(step, args.steps, args.warmup, stream)
     es = 2 if w.dtype == si.BF16 else 4
     elems = w.batch * w.L * w.dim
     slots_el = bwd_valu_slots(w.N, w.gate, es) + (algorithmic_valu_slots(w.N, w.gate, es)
@@ -425,7 +445,8 @@ def bench_bwd(w, args):
         "config": {"workload": w.name, "pass": args.which, "batch": w.batch, "L": w.L,
                    "dim": w.dim,
                    "N": w.N, "gate": w.gate},
-        "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms))},
+        "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms)),
+                    "timed_quarters": quarters},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_SLOTS / 1e9,
                      "unit": "G VALU lane-slots/s", "frac": achieved * 1e9 / VALU_PEAK_SLOTS,
                      "traffic": None,
@@ -471,6 +492,9 @@ def main():
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fwdbwd"), default="fwd")
     ap.add_argument("--variant", default="", help="variants: zoh, rev, convK (fwd or bwd)")
+    ap.add_argument("--a", dest="a_form", choices=("s4d", "general"), default="s4d",
+                    help="A = -(n+1) (S4D-real: the power-chain A_bar) or a perturbed, "
+                         "general A (A_bar by one exp2 per (t, n))")
     args = ap.parse_args()
 
     import selscan_inputs as si
@@ -499,6 +523,11 @@ def main():
 
     dev = torch.device("cuda:0")
     inp, sets = make_inputs(w, dev, args.rotate)
+    general_a = args.a_form == "general"
+    if general_a:
+        inp.A = si.perturbed_A(w.dim, w.N, w.seed)
+        for t in sets:
+            t["A"] = torch.from_numpy(inp.A).to(dev)
     es = 2 if w.dtype == si.BF16 else 4
     ys = [torch.empty((w.batch, w.L, w.dim), dtype=sets[0]["u"].dtype, device=dev)
           for _ in range(args.rotate)]
@@ -528,12 +557,13 @@ def main():
                        y=ys[i % args.rotate], h_last=hls[i % args.rotate],
                        workspace=wss[i % args.rotate], stream=stream)
 
-    wall, call_mean, call_ms = timed_steps(step, args.steps, args.warmup, stream)
+    wall, call_mean, call_ms, quarters = timed_steps(step, args.steps, args.warmup, stream)
 
     elems = w.batch * w.L * w.dim
     ms_per_step = 1e3 * wall / args.steps
     abytes = algorithmic_bytes(w.batch, w.L, w.dim, w.N, es, w.gate, w.want_last_state)
-    slots = algorithmic_valu_slots(w.N, w.gate, es) * elems
+    slots_el = algorithmic_valu_slots(w.N, w.gate, es, general_a)
+    slots = slots_el * elems
     achieved = slots / (call_mean * 1e-3) / 1e9
     peak = VALU_PEAK_SLOTS / 1e9
     result = {
@@ -551,29 +581,33 @@ def main():
         "data": "synthetic (seeded; u,B,C,z ~ N(0,1), Delta_raw ~ N(0,0.5^2), "
                 "dt log-uniform [1e-3,0.1], A=-(n+1), D=1)",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "dim": w.dim, "N": w.N,
-                   "gate": w.gate, "state": "fp32", "rotating_input_sets": args.rotate},
+                   "gate": w.gate, "state": "fp32", "rotating_input_sets": args.rotate,
+                   "A": ("general: -(n+1) exp(N(0, 0.25^2)) per (d, n)" if general_a
+                         else "S4D-real: -(n+1)"),
+                   "abar": "exp2_per_state" if general_a else "power_chain_s4d_real"},
         **({"variant": args.variant} if args.variant else {}),
         "hbm_gbps": abytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": abytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "call_ms": {"mean": call_mean,
+        "call_ms": {"mean": call_mean, "timed_quarters": quarters,
                     "single_call": {"p10": float(np.percentile(call_ms, 10)),
                                     "p50": float(np.median(call_ms)),
                                     "p90": float(np.percentile(call_ms, 90)),
                                     "calls": len(call_ms)}},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
                      "unit": "G VALU lane-slots/s", "frac": achieved / peak,
-                     "traffic": load_traffic(w.name),
+                     "traffic": None if general_a else load_traffic(w.name),
                      "kernel": "selscan_fwd call (summary, carry and main passes)",
-                     "algorithmic_slots_per_element": algorithmic_valu_slots(w.N, w.gate, es),
+                     "algorithmic_slots_per_element": slots_el,
                      "algorithmic_bytes_per_call": abytes,
-                     "hbm_gbps_of_call": abytes / (call_mean * 1e-3) / 1e9},
+                     "hbm_gbps_of_call": abytes / (call_mean * 1e-3) / 1e9,
+                     "hbm_frac_of_call": abytes / (call_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS},
     }
     if args.variant:
         result["roofline"]["traffic"] = None
         result["roofline"]["kernel"] = "selscan_fwd_ex call (%s); slots of the default path" \
             % args.variant
     result["device_copy_gbps"] = device_copy_gbps(dev)
-    if not args.no_cpu and not args.variant:
+    if not args.no_cpu and not args.variant and not general_a:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)
 

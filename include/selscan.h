@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 5
+#define SELSCAN_ABI_VERSION 6
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -105,7 +105,9 @@ enum selscan_status {
                                     aligned                                          */
     SELSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
     SELSCAN_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer        */
-    SELSCAN_ERR_HIP = 7          /* a HIP runtime call failed                        */
+    SELSCAN_ERR_HIP = 7,         /* a HIP runtime call failed                        */
+    SELSCAN_ERR_TIMEOUT = 8      /* selscan_fwd_status: a bounded wait in a kernel
+                                    gave up, the outputs of that call are invalid    */
 };
 
 /* SELSCAN_ABI_VERSION of the built library. */
@@ -119,6 +121,24 @@ int selscan_last_hip_error(void);
 
 /* Nonzero if N is a compiled state size (4, 8, 16, 32 and 64 are built). */
 int selscan_supports_n(int64_t N);
+
+/*
+ * Completion status of the last selscan_fwd queued on `stream` with this
+ * workspace.  Only the single-pass plan with decoupled look-back
+ * (SELSCAN_FORCE_PLAN=lookback in the environment; the chunked scan with a
+ * carry passed between blocks of the paper walkthrough (m.lqnn.cn) §3.2)
+ * has waits between waves; each is bounded (SELSCAN_LOOKBACK_SPIN_LIMIT polls
+ * if set, else about 2^20).  A wave whose wait gives up sets a status word
+ * in the workspace and poisons its state with NaN, so its sequence part and
+ * every later part of its channel group come out NaN.
+ *
+ * Under that plan this call waits for `stream`, reads the word and returns
+ * SELSCAN_ERR_TIMEOUT if it is set, SELSCAN_OK otherwise (SELSCAN_ERR_HIP if
+ * the read fails; SELSCAN_ERR_NULL for a NULL workspace).  Under any other
+ * plan nothing can time out: it returns SELSCAN_OK at once, touching nothing.
+ * Unlike the compute calls, it synchronises.
+ */
+int selscan_fwd_status(const void *workspace, void *stream);
 
 /*
  * Bytes of device workspace selscan_fwd needs for this shape (0 is possible:
@@ -284,7 +304,9 @@ int selscan_bwd(const void *u, const void *delta, const float *A,
  * SELSCAN_FLAG_REUSE_FWD_STATE (in flags, with REVERSE or alone; not with
  * ZOH_EXACT or conv_width > 0, SELSCAN_ERR_UNSUPPORTED): the workspace is the
  * one the matching forward last ran in (selscan_fwd, or selscan_fwd_ex with
- * the same REVERSE flag and no other variant) with the same u, delta, A, Bm,
+ * the same REVERSE flag and no other variant, under the default plan: with
+ * SELSCAN_FORCE_PLAN set to another plan the flag is SELSCAN_ERR_UNSUPPORTED,
+ * since that forward leaves another layout) with the same u, delta, A, Bm,
  * delta_bias, delta_softplus, h0 and sizes, and still holds that forward's
  * sequence-part summaries and part entry states, which the backward then
  * reads instead of recomputing (the forward's summary and carry passes).

@@ -55,6 +55,8 @@ def lib():
         L.selscan_last_hip_error.argtypes = []
         L.selscan_supports_n.restype = I
         L.selscan_supports_n.argtypes = [I64]
+        L.selscan_fwd_status.restype = I
+        L.selscan_fwd_status.argtypes = [P, P]
         L.selscan_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
         L.selscan_fwd.restype = I
@@ -115,6 +117,15 @@ def _ptr(t: Optional[torch.Tensor]):
 def _stream(device, stream):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def selscan_fwd_status(workspace: torch.Tensor, stream=None) -> None:
+    """Waits for ``stream`` and raises SelscanError (SELSCAN_ERR_TIMEOUT) if a
+    bounded wait of the look-back plan gave up during the last forward in
+    ``workspace``; returns at once under any other plan."""
+    st = lib().selscan_fwd_status(_ptr(workspace), _stream(workspace.device, stream))
+    if st != 0:
+        raise SelscanError(st, "selscan_fwd_status", lib().selscan_last_hip_error())
 
 
 def selscan_fwd_workspace_bytes(batch: int, L: int, dim: int, N: int, dtype: int) -> int:

@@ -10,7 +10,9 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import hashlib
 import os
+import shutil
 import subprocess
 import sys
 import tempfile
@@ -48,8 +50,26 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False, extra_flags=(), jobs: int = 0) -> str:
-    """Compile every csrc/*.hip to an object (in parallel), then link."""
+# Object cache of incremental builds (git-ignored): one object per source,
+# keyed by the source, every header it could include and the flags.
+CACHE = os.path.join(os.path.dirname(PKG), "_build", "objs")
+
+
+def _unit_key(src, flags):
+    h = hashlib.sha256()
+    h.update(" ".join(flags).encode())
+    headers = sorted(glob.glob(os.path.join(CSRC, "*.hpp")) +
+                     glob.glob(os.path.join(os.path.dirname(PKG), "include", "*.h")))
+    for path in [src] + headers:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:24]
+
+
+def build(verbose: bool = False, extra_flags=(), jobs: int = 0, incremental: bool = False) -> str:
+    """Compile every csrc/*.hip to an object (in parallel), then link.  With
+    ``incremental``, objects whose source, headers and flags are unchanged
+    come from the object cache (the default compiles everything)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     if jobs <= 0:
         try:
@@ -58,13 +78,23 @@ def build(verbose: bool = False, extra_flags=(), jobs: int = 0) -> str:
             jobs = os.cpu_count() or 1
         jobs = max(1, min(jobs, 16))
     compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    flags = [*compile_flags, *extra_flags]
     with tempfile.TemporaryDirectory(prefix="selscan_build_") as tmpdir:
         objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in sources()]
-        cmds = [[hipcc, *compile_flags, *extra_flags, "-c", src, "-o", obj]
-                for src, obj in zip(sources(), objs)]
+        cmds, cached = [], []
+        for src, obj in zip(sources(), objs):
+            key = os.path.join(CACHE, "%s.%s.o" % (os.path.basename(src), _unit_key(src, flags)))
+            if incremental and os.path.exists(key):
+                shutil.copyfile(key, obj)
+                continue
+            cmds.append([hipcc, *flags, "-c", src, "-o", obj])
+            cached.append((obj, key))
         with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
+        os.makedirs(CACHE, exist_ok=True)
+        for obj, key in cached:
+            shutil.copyfile(obj, key)
         tmp = LIB + ".tmp%d" % os.getpid()
         _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
@@ -72,5 +102,5 @@ def build(verbose: bool = False, extra_flags=(), jobs: int = 0) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))
     sys.exit(0)

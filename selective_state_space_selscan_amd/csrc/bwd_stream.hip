@@ -74,6 +74,8 @@ __global__ __launch_bounds__(kLanes * kColsumWaves) void bwd_colsum_kernel(Colsu
 
 void ColsumJobs::add(const float *in, float *out, int64_t P, int64_t K)
 {
+    if (!out)
+        return;   // an optional gradient the caller does not want (NULL = skip)
     if (n >= kMaxColsumJobs) {
         n = kMaxColsumJobs + 1;   // the table is full: launch_colsums refuses it
         return;
@@ -90,8 +92,13 @@ void ColsumJobs::add(const float *in, float *out, int64_t P, int64_t K)
 
 hipError_t launch_colsums(const ColsumJobs &jobs, hipStream_t s)
 {
-    if (jobs.n < 1 || jobs.n > kMaxColsumJobs || jobs.blocks > 0x7fffffff)
+    if (jobs.n > kMaxColsumJobs || jobs.blocks > 0x7fffffff)
         return hipErrorInvalidValue;
+    for (int q = 0; q < jobs.n; ++q)
+        if (!jobs.j[q].in || !jobs.j[q].out || jobs.j[q].P <= 0 || jobs.j[q].K <= 0)
+            return hipErrorInvalidValue;
+    if (jobs.n == 0)
+        return hipSuccess;
     hipLaunchKernelGGL(bwd_colsum_kernel, dim3((unsigned)jobs.blocks),
                        dim3(kLanes * kColsumWaves), 0, s, jobs);
     return hipGetLastError();

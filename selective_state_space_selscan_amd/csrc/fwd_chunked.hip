@@ -1,4 +1,5 @@
-// Chunked selective-scan forward for gfx950 (the fast path).
+// Chunked selective-scan forward for gfx950 (an ablation plan, SELSCAN_FORCE_PLAN=chunked;
+// measured slower than the streaming plan, which is the default).
 //
 // What it computes is the S6 recurrence of the Mamba tutorial (pwwt.cn)
 // §3.1-§3.2 and §4.2: Delta_t = softplus(Delta_raw + bias), A_bar = exp(Delta_t A)

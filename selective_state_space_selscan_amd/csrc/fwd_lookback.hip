@@ -15,7 +15,10 @@
 // between and the walk moves one part further back.  Parts are handed out in
 // the order the waves start (a ticket counter), so a wave only waits for
 // waves that started before it and never wait for it: every wait ends.  The
-// waits are still bounded (kSpinLimit polls).
+// waits are still bounded (a poll limit, kSpinLimit by default).  A wave
+// whose wait gives up sets the status word of the workspace (read back by
+// selscan_fwd_status) and poisons its state with NaN, so that its part and
+// every later part of its group come out NaN rather than silently wrong.
 //
 // Memory ordering: a part's data is written with device-coherent (agent-scope)
 // atomic stores; once they have completed (s_waitcnt) the part's flag is set
@@ -38,6 +41,7 @@ constexpr int kSpinLimit = 1 << 20;
 
 struct LookbackWs {
     unsigned *ticket;   // one counter, zero at launch
+    unsigned *status;   // zero at launch; bit 0 set by a wave whose wait gave up
     unsigned *flags;    // (groups, parts), zero at launch
     float *agg;         // (groups, parts, N + 1, 64): sum of Delta, end state from zero
     float *incl;        // (groups, parts, N, 64): state at the end of the part
@@ -50,11 +54,11 @@ __global__ __launch_bounds__(256) void lookback_clear_kernel(unsigned *p, int64_
         p[i] = 0u;
 }
 
-// Polls a flag (relaxed) until it is nonzero or kSpinLimit polls pass.
-__device__ __forceinline__ unsigned poll_flag(unsigned *f)
+// Polls a flag (relaxed) until it is nonzero or `limit` polls pass (then 0).
+__device__ __forceinline__ unsigned poll_flag(unsigned *f, int limit)
 {
     unsigned v = 0;
-    for (int it = 0; it < kSpinLimit; ++it) {
+    for (int it = 0; it < limit; ++it) {
         v = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         if (v != 0)
@@ -112,7 +116,8 @@ void fwd_lookback_kernel(const TIO *__restrict__ u, const TIO *__restrict__ delt
                          const TIO *__restrict__ Cm, const float *__restrict__ D_skip,
                          const float *__restrict__ delta_bias, int delta_softplus,
                          const float *__restrict__ h0, float *__restrict__ h_last, LookbackWs ws,
-                         int64_t L, int64_t dim, int64_t groups, int parts, int64_t part_len)
+                         int64_t L, int64_t dim, int64_t groups, int parts, int64_t part_len,
+                         int spin_limit)
 {
     __shared__ unsigned s_ticket;
     if (threadIdx.x == 0)
@@ -205,11 +210,22 @@ void fwd_lookback_kernel(const TIO *__restrict__ u, const TIO *__restrict__ delt
     // Find how far back to look with relaxed polls, then acquire once and
     // read the states: an acquire costs an L2 invalidation on this chip.
     int q_stop = -1;   // the part whose inclusive state ends the walk (-1: h0)
+    bool gave_up = false;
     for (int q = part - 1; q >= 0; --q) {
-        if (poll_flag(&ws.flags[grp * parts + q]) == kFlagInclusive) {
+        const unsigned f = poll_flag(&ws.flags[grp * parts + q], spin_limit);
+        if (f == 0) {
+            gave_up = true;   // part q never published within the limit
+            break;
+        }
+        if (f == kFlagInclusive) {
             q_stop = q;
             break;
         }
+    }
+    if (gave_up) {
+        if (lane == 0)
+            __hip_atomic_fetch_or(ws.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        q_stop = part - 1;   // read nothing unpublished below: the state is poisoned instead
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // keeps the data reads below
     if (q_stop >= 0) {
@@ -232,9 +248,10 @@ void fwd_lookback_kernel(const TIO *__restrict__ u, const TIO *__restrict__ delt
     {
         float E[N];
         decay<N>(E, Sa, pow_path, A2, c.A2_0);
+        const float poison = gave_up ? __builtin_nanf("") : 0.0f;
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            h[n] = fmaf(E[n], hin[n], xa[n]);
+            h[n] = fmaf(E[n], hin[n], xa[n]) + poison;
     }
 
     // 3. this part's inclusive state, for the parts after it
@@ -274,6 +291,8 @@ void fwd_lookback_kernel(const TIO *__restrict__ u, const TIO *__restrict__ delt
     }
 }
 
+// The ticket counter and the status word lead the workspace (words 0 and 1
+// of the aligned base: selscan_fwd_status reads word 1), then the flags.
 struct LookbackLayout {
     size_t flags, agg, incl, total;   // byte offsets from the aligned base
 };
@@ -285,22 +304,24 @@ LookbackLayout lookback_layout(const StreamPlan &p, int64_t N)
     LookbackLayout w;
     const size_t slots = (size_t)p.groups * p.parts;
     w.flags = 0;
-    w.agg = align256((1 + slots) * sizeof(unsigned));
+    w.agg = align256((kLookbackFlagsOffset + slots) * sizeof(unsigned));
     w.incl = align256(w.agg + slots * (N + 1) * kLanes * 4);
     w.total = align256(w.incl + slots * N * kLanes * 4) + 256;
     return w;
 }
 
 template <int N, typename TIO>
-hipError_t launch_n(const FwdArgs &a, const StreamPlan &p, char *base, hipStream_t s)
+hipError_t launch_n(const FwdArgs &a, const StreamPlan &p, char *base, int spin_limit,
+                    hipStream_t s)
 {
     const LookbackLayout l = lookback_layout(p, N);
     LookbackWs ws;
     ws.ticket = (unsigned *)(base + l.flags);
-    ws.flags = ws.ticket + 1;
+    ws.status = ws.ticket + kLookbackStatusWord;
+    ws.flags = ws.ticket + kLookbackFlagsOffset;
     ws.agg = (float *)(base + l.agg);
     ws.incl = (float *)(base + l.incl);
-    const int64_t nflags = 1 + p.groups * p.parts;
+    const int64_t nflags = kLookbackFlagsOffset + p.groups * p.parts;
     hipLaunchKernelGGL(lookback_clear_kernel, dim3((unsigned)((nflags + 255) / 256)), dim3(256),
                        0, s, ws.ticket, nflags);
     hipError_t e = hipGetLastError();
@@ -311,19 +332,19 @@ hipError_t launch_n(const FwdArgs &a, const StreamPlan &p, char *base, hipStream
                        (const TIO *)a.u, (const TIO *)a.delta, (const TIO *)a.z, (TIO *)a.y, a.A,
                        (const TIO *)a.Bm, (const TIO *)a.Cm, a.D_skip, a.delta_bias,
                        a.delta_softplus, a.h0, a.h_last, ws, a.L, a.dim, p.groups, p.parts,
-                       p.part_len);
+                       p.part_len, spin_limit);
     return hipGetLastError();
 }
 
 template <typename TIO>
-hipError_t launch_t(const FwdArgs &a, const StreamPlan &p, char *base, hipStream_t s)
+hipError_t launch_t(const FwdArgs &a, const StreamPlan &p, char *base, int spin, hipStream_t s)
 {
     switch (a.N) {
-    case 4: return launch_n<4, TIO>(a, p, base, s);
-    case 8: return launch_n<8, TIO>(a, p, base, s);
-    case 16: return launch_n<16, TIO>(a, p, base, s);
-    case 32: return launch_n<32, TIO>(a, p, base, s);
-    case 64: return launch_n<64, TIO>(a, p, base, s);
+    case 4: return launch_n<4, TIO>(a, p, base, spin, s);
+    case 8: return launch_n<8, TIO>(a, p, base, spin, s);
+    case 16: return launch_n<16, TIO>(a, p, base, spin, s);
+    case 32: return launch_n<32, TIO>(a, p, base, spin, s);
+    case 64: return launch_n<64, TIO>(a, p, base, spin, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -335,12 +356,13 @@ size_t fwd_lookback_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64
     return lookback_layout(make_stream_plan(batch, L, dim), N).total;
 }
 
-hipError_t launch_fwd_lookback(const FwdArgs &a, hipStream_t stream)
+hipError_t launch_fwd_lookback(const FwdArgs &a, int spin_limit, hipStream_t stream)
 {
     const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim);
     char *base = (char *)(((uintptr_t)a.workspace + 255) & ~(uintptr_t)255);
-    return a.dtype == 1 ? launch_t<uint16_t>(a, p, base, stream)
-                        : launch_t<float>(a, p, base, stream);
+    const int spin = spin_limit >= 0 ? spin_limit : kSpinLimit;
+    return a.dtype == 1 ? launch_t<uint16_t>(a, p, base, spin, stream)
+                        : launch_t<float>(a, p, base, spin, stream);
 }
 
 } // namespace selscan

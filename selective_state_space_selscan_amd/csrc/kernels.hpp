@@ -43,10 +43,8 @@ struct StepArgs {
     int dtype;
 };
 
-// Serial forward: one lane per (batch, channel), whole sequence in-lane.
-hipError_t launch_fwd_serial(const FwdArgs &a, hipStream_t stream);
-
-// Chunked forward (the fast path): workspace bytes it needs, and the launch.
+// Chunked forward (ablation: wave segments of a chunk exchange their
+// aggregates through LDS): workspace bytes it needs, and the launch.
 size_t fwd_chunked_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_chunked(const FwdArgs &a, hipStream_t stream);
 
@@ -72,8 +70,13 @@ size_t fwd_stream_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t
 hipError_t launch_fwd_stream(const FwdArgs &a, hipStream_t stream);
 
 // Single-pass streaming forward with decoupled look-back (same plan).
+// spin_limit: polls before a wait gives up (< 0: the default).  Word
+// kLookbackStatusWord of the aligned workspace is nonzero after a call in
+// which some wait gave up.
+constexpr int kLookbackStatusWord = 1;
+constexpr int kLookbackFlagsOffset = 2;   // words: ticket, status, then the flags
 size_t fwd_lookback_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
-hipError_t launch_fwd_lookback(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_fwd_lookback(const FwdArgs &a, int spin_limit, hipStream_t stream);
 
 // Variants of the streaming forward (same plan and workspace).
 constexpr int kFwdFlagZohExact = 1;

@@ -41,15 +41,25 @@ bool grids_fit(int64_t batch, int64_t L, int64_t dim, int64_t N)
 
 // Forward plans.  Default: the two-pass streaming kernel.  SELSCAN_FORCE_PLAN
 // = lookback selects the single-pass streaming kernel with decoupled
-// look-back; = chunked or = serial the workgroup-chunked or the
-// one-lane-per-channel kernel (ablations; all compute the same recurrence).
-enum Plan { PLAN_STREAM, PLAN_LOOKBACK, PLAN_CHUNKED, PLAN_SERIAL };
+// look-back; = chunked the workgroup-chunked kernel (ablations; both compute
+// the same recurrence).
+enum Plan { PLAN_STREAM, PLAN_LOOKBACK, PLAN_CHUNKED };
+
+// Polls before a look-back wait gives up: SELSCAN_LOOKBACK_SPIN_LIMIT (a
+// count >= 0), else the kernel's default (-1).
+int lookback_spin_limit()
+{
+    const char *e = getenv("SELSCAN_LOOKBACK_SPIN_LIMIT");
+    if (!e || !*e)
+        return -1;
+    char *end = nullptr;
+    const long v = strtol(e, &end, 10);
+    return (end && *end == 0 && v >= 0 && v <= 0x7fffffff) ? (int)v : -1;
+}
 
 Plan forced_plan()
 {
     const char *e = getenv("SELSCAN_FORCE_PLAN");
-    if (e && strcmp(e, "serial") == 0)
-        return PLAN_SERIAL;
     if (e && strcmp(e, "chunked") == 0)
         return PLAN_CHUNKED;
     if (e && strcmp(e, "lookback") == 0)
@@ -152,12 +162,11 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
     if (ext)
         return finish_launch(selscan::launch_fwd_stream_ext(a, *ext, (hipStream_t)stream));
     switch (forced_plan()) {
-    case PLAN_SERIAL:
-        return finish_launch(selscan::launch_fwd_serial(a, (hipStream_t)stream));
     case PLAN_CHUNKED:
         return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
     case PLAN_LOOKBACK:
-        return finish_launch(selscan::launch_fwd_lookback(a, (hipStream_t)stream));
+        return finish_launch(
+            selscan::launch_fwd_lookback(a, lookback_spin_limit(), (hipStream_t)stream));
     default:
         return finish_launch(selscan::launch_fwd_stream(a, (hipStream_t)stream));
     }
@@ -252,11 +261,31 @@ const char *selscan_status_string(int status)
     case SELSCAN_ERR_WORKSPACE: return "workspace missing or too small";
     case SELSCAN_ERR_ALIAS: return "an output overlaps an input";
     case SELSCAN_ERR_HIP: return "a HIP runtime call failed";
+    case SELSCAN_ERR_TIMEOUT: return "a bounded wait inside a kernel gave up; outputs are invalid";
     default: return "unknown status";
     }
 }
 
 int selscan_last_hip_error(void) { return g_last_hip_error; }
+
+int selscan_fwd_status(const void *workspace, void *stream)
+{
+    if (forced_plan() != PLAN_LOOKBACK)
+        return SELSCAN_OK;   // no other plan has a wait that can give up
+    if (!workspace)
+        return SELSCAN_ERR_NULL;
+    const unsigned *base = (const unsigned *)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    unsigned word = 0;
+    hipError_t e = hipMemcpyAsync(&word, base + selscan::kLookbackStatusWord, sizeof(word),
+                                  hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return SELSCAN_ERR_HIP;
+    }
+    return word ? SELSCAN_ERR_TIMEOUT : SELSCAN_OK;
+}
 
 int selscan_supports_n(int64_t N) { return supported_n(N) ? 1 : 0; }
 
@@ -345,6 +374,9 @@ int selscan_bwd_ex(const void *u, const void *delta, const float *A, const void 
     // the default plan: the plain forward and the reverse-alone variant
     if ((flags & SELSCAN_FLAG_REUSE_FWD_STATE) &&
         ((flags & SELSCAN_FLAG_ZOH_EXACT) || conv_width > 0))
+        return SELSCAN_ERR_UNSUPPORTED;
+    // a forced forward plan leaves another workspace layout (or none)
+    if ((flags & SELSCAN_FLAG_REUSE_FWD_STATE) && forced_plan() != PLAN_STREAM)
         return SELSCAN_ERR_UNSUPPORTED;
     selscan::FwdExt e;
     e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |

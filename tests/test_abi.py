@@ -26,7 +26,7 @@ no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer tests run 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "selscan.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_WS, ERR_ALIAS, ERR_HIP = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_WS, ERR_ALIAS, ERR_HIP, ERR_TIMEOUT = range(9)
 
 
 def header_functions():
@@ -52,8 +52,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_supported_n():
     L = ss.lib()
-    for s in range(8):
+    for s in range(9):
         assert len(L.selscan_status_string(s)) > 0
+        assert L.selscan_status_string(s) != b"unknown status"
     assert L.selscan_status_string(99) == b"unknown status"
     for n in (4, 8, 16, 32, 64):
         assert L.selscan_supports_n(n) == 1
@@ -271,6 +272,33 @@ def test_bwd_ex_rejects_invalid_arguments(name, kw, status):
     L = ss.lib()
     assert L.selscan_bwd_ex(*bwd_ex_args(**kw)) == status
     assert L.selscan_last_hip_error() == 0
+
+
+@no_gpu_only
+@pytest.mark.parametrize("plan", ["lookback", "chunked"])
+def test_bwd_ex_refuses_reuse_under_forced_plan(monkeypatch, plan):
+    """A forward under another plan leaves another workspace layout, so the
+    backward cannot read its part state from it."""
+    monkeypatch.setenv("SELSCAN_FORCE_PLAN", plan)
+    L = ss.lib()
+    for flags in (4, 4 | 2):
+        assert L.selscan_bwd_ex(*bwd_ex_args(flags=flags)) == ERR_UNSUP
+        assert L.selscan_last_hip_error() == 0
+
+
+def test_fwd_status_without_lookback_plan_touches_nothing(monkeypatch):
+    """Only the look-back plan has waits that can give up; under any other
+    plan the status call returns OK without reading the workspace (a fake
+    address here) or touching the stream."""
+    L = ss.lib()
+    for plan in (None, "chunked"):
+        if plan is None:
+            monkeypatch.delenv("SELSCAN_FORCE_PLAN", raising=False)
+        else:
+            monkeypatch.setenv("SELSCAN_FORCE_PLAN", plan)
+        assert L.selscan_fwd_status(fake(12), None) == OK
+    monkeypatch.setenv("SELSCAN_FORCE_PLAN", "lookback")
+    assert L.selscan_fwd_status(None, None) == ERR_NULL
 
 
 def test_flag_constants_match_header():

@@ -1,9 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
 Every workload and edge case compares the kernel output element by element
-with the oracle on the same seeded inputs.  The large workloads use a sample
-of channels on the oracle side: channels are independent in the scan, so the
-oracle run on the sliced inputs yields exactly those channels' outputs.
+with the oracle on the same seeded inputs, every channel of every workload
+included (the long sequence, the large layer and all 1024 decode steps).
 
 Because D*u dominates y (the scan part is a small fraction of it), every
 workload is also run with D_skip = 0 and no gate, and its final state h_L is
@@ -58,8 +57,8 @@ def sample_channels(dim, k, seed=0):
     return np.sort(np.unique(c))
 
 
-WORKLOAD_SAMPLES = {"tiny_f32": None, "mamba130m_layer": None, "long_seq": 48,
-                    "large_layer": 96}
+WORKLOAD_SAMPLES = {"tiny_f32": None, "mamba130m_layer": None, "long_seq": None,
+                    "large_layer": None}
 
 
 @pytest.mark.parametrize("name", list(WORKLOAD_SAMPLES))
@@ -75,11 +74,11 @@ def test_workload_parity(device, name, variant):
 
 def test_decode_workload(device):
     """1024 single-token steps on the resident fp32 state (batch 256, D 5120,
-    N 16), checked against the oracle's recurrence every 64 steps on a sample
-    of channels (all batch rows)."""
+    N 16), checked against the oracle's recurrence every 64 steps: y and the
+    whole state, every channel and batch row."""
     w = si.WORKLOADS["decode"]
     A, D, bias = si.decode_params(w)
-    ch = sample_channels(w.dim, 48, seed=1)
+    ch = np.arange(w.dim)
     tA, tD, tb = (torch.from_numpy(x).to(device) for x in (A, D, bias))
     state = torch.zeros((w.batch, w.dim, w.N), dtype=torch.float32, device=device)
     ostate = np.zeros((w.batch, len(ch), w.N), dtype=np.float64)

@@ -105,3 +105,32 @@ def test_lookback_repeated_calls_agree(device):
                          inp.D_skip, inp.z.value, inp.delta_bias, True, inp.h0)
     for y, h in outs:
         assert rel_err(to_np(y), ey) <= TOL["bf16"] and rel_err(to_np(h), ehL) <= TOL["bf16"]
+
+
+def test_lookback_gave_up_wait_is_reported(device, monkeypatch):
+    """With a poll limit of 0 every wait of a part after the first gives up at
+    once (no wave ever waits, so every kernel still runs to its end): the
+    status call reports SELSCAN_ERR_TIMEOUT and those parts come out NaN.
+    With the default limit the same call is correct and reports OK."""
+    inp = si.make_fwd_inputs(2, 3000, 128, 16, si.BF16, True, seed=1490, h0=True)
+    t = si.fwd_tensors(inp, device)
+    code = ss.SELSCAN_BF16
+    ws = torch.empty(ss.selscan_fwd_workspace_bytes(2, 3000, 128, 16, code), dtype=torch.uint8,
+                     device=device)
+    monkeypatch.setenv("SELSCAN_LOOKBACK_SPIN_LIMIT", "0")
+    say("case lookback spin limit 0")
+    y = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                       t["delta_bias"], True, t["h0"], workspace=ws)
+    with pytest.raises(ss.SelscanError) as e:
+        ss.selscan_fwd_status(ws)
+    assert e.value.status == 8   # SELSCAN_ERR_TIMEOUT
+    yn = to_np(y)
+    assert np.isnan(yn[:, -1]).all()          # the last part is poisoned
+    assert not np.isnan(yn[:, 0]).any()       # the first part never waits
+    monkeypatch.delenv("SELSCAN_LOOKBACK_SPIN_LIMIT")
+    say("case lookback default spin limit")
+    y = ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                       t["delta_bias"], True, t["h0"], workspace=ws)
+    ss.selscan_fwd_status(ws)   # raises on a timeout
+    ey, _ = oracle.fwd_inputs(inp)
+    assert rel_err(to_np(y), ey) <= TOL["bf16"]
