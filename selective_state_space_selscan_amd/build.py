@@ -51,16 +51,28 @@ def _run(cmd, verbose):
 
 
 # Object cache of incremental builds (git-ignored): one object per source,
-# keyed by the source, every header it could include and the flags.
+# keyed by the source, the repository headers it includes and the flags.
 CACHE = os.path.join(os.path.dirname(PKG), "_build", "objs")
+
+
+def _local_includes(path, seen):
+    """The repository headers ``path`` includes, transitively (quoted
+    includes resolved against the including file's directory)."""
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("#include \""):
+                inc = os.path.normpath(os.path.join(os.path.dirname(path), line.split('"')[1]))
+                if os.path.exists(inc) and inc not in seen:
+                    seen.add(inc)
+                    _local_includes(inc, seen)
+    return seen
 
 
 def _unit_key(src, flags):
     h = hashlib.sha256()
     h.update(" ".join(flags).encode())
-    headers = sorted(glob.glob(os.path.join(CSRC, "*.hpp")) +
-                     glob.glob(os.path.join(os.path.dirname(PKG), "include", "*.h")))
-    for path in [src] + headers:
+    for path in [src] + sorted(_local_includes(src, set())):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:24]

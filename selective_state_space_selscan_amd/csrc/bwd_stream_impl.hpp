@@ -242,7 +242,7 @@ __device__ __forceinline__ void adjoint_summary_part(const TIO *delta, const TIO
             const float zt = raw_f<TIO>(A.z[i]);
             const float dypre = raw_f<TIO>(A.dy[i]) * (z ? silu(zt) : 1.0f);
             if (POW) {
-                P *= hw_exp2(dt * c.A2_0);
+                P *= exp2_decay(dt * c.A2_0, tag<TIO>());
                 float pw = P * dypre;
 #pragma unroll
                 for (int n = 0; n < N; ++n) {
@@ -252,7 +252,7 @@ __device__ __forceinline__ void adjoint_summary_part(const TIO *delta, const TIO
             } else {
 #pragma unroll
                 for (int n = 0; n < N; ++n) {
-                    Pn[n] *= hw_exp2(dt * A2[n]);
+                    Pn[n] *= exp2_decay(dt * A2[n], tag<TIO>());
                     v[n] = fmaf(Pn[n] * dypre, row_val<N>(crow, n), v[n]);
                 }
             }
@@ -513,12 +513,12 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
             float dt = c.softplus ? sp : xr;
             dt = i < rows ? dt : 0.0f;
             const float du = dt * ut;
-            const float r = POW ? hw_exp2(dt * c.A2_0) : 0.0f;
+            const float r = POW ? exp2_decay(dt * c.A2_0, tag<TIO>()) : 0.0f;
             float pw = 1.0f;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float x2 = dt * A2[n];
-                const float a = POW ? (pw *= r) : hw_exp2(x2);
+                const float a = POW ? (pw *= r) : exp2_decay(x2, tag<TIO>());
                 const float bu = ZOH ? stream::zoh_coeff(dt, x2, a, invA[n]) *
                                            (ut * row_val<N>(brow, n))
                                      : du * row_val<N>(brow, n);
@@ -558,7 +558,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
         const float du_a = active ? du : 0.0f;
         const float ut_a = active ? ut : 0.0f;
         const float dypre_a = active ? dypre : 0.0f;
-        const float r = POW ? hw_exp2(dt * c.A2_0) : 0.0f;
+        const float r = POW ? exp2_decay(dt * c.A2_0, tag<TIO>()) : 0.0f;
         float pw = 1.0f;
         float ypre = c.Dd * ut, sLB = 0.0f, wA = 0.0f, wE = 0.0f;
 #pragma unroll
@@ -569,7 +569,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
             ypre = fmaf(Cn, hn, ypre);
             float a = 0.0f;
             if constexpr (ZOH || !FIXED)
-                a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
+                a = POW ? (pw *= r) : exp2_decay(dt * A2[n], tag<TIO>());
             if constexpr (ZOH) {
                 const float x2 = dt * A2[n];
                 const float cn = stream::zoh_coeff(dt, x2, a, invA[n]);
@@ -592,7 +592,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
             // this lane's terms of dC_t[n]; row n of the LDS tiles
             ldsC[n * kLdsStride + lane] = dypre_a * hn;
             if constexpr (!ZOH && FIXED)
-                a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
+                a = POW ? (pw *= r) : exp2_decay(dt * A2[n], tag<TIO>());
             g[n] = a * lam;
         }
         // sum_n A[n] w[n]: A2 carries log2(e), the structured chain A[d,0]

@@ -40,6 +40,33 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// 2^x for the decay of one step, x = Delta A log2(e) <= 0, with fp32-level
+// accuracy where it matters.  v_exp_f32 is accurate to about 1 ulp, but its
+// errors do not average out: when 2^x is close to 1 (a slow decay, small
+// Delta |A|) the product of many steps' decays, which a state carries for
+// about 1 / (Delta |A|) steps, picks up their sum (measured: a 1e-4 error in
+// y after 96 steps of an fp32 sequence whose initial state decays slowly).
+// For |x| < 1/16 the Taylor series of 2^x - 1 in x (degree 5, truncation
+// below 1e-10 relative) is added to 1, one rounding to nearest; elsewhere the
+// hardware exp2 is used (1 - 2^x > 0.04 there, so an ulp of 2^x is small
+// against the decay it describes).
+__device__ __forceinline__ float exp2_decay_accurate(float x) {
+    constexpr float c1 = kLn2;
+    constexpr float c2 = kLn2 * kLn2 / 2.0f;
+    constexpr float c3 = kLn2 * kLn2 * kLn2 / 6.0f;
+    constexpr float c4 = kLn2 * kLn2 * kLn2 * kLn2 / 24.0f;
+    constexpr float c5 = kLn2 * kLn2 * kLn2 * kLn2 * kLn2 / 120.0f;
+    const float p = fmaf(x, fmaf(x, fmaf(x, fmaf(x, c5, c4), c3), c2), c1);
+    const float series = fmaf(x, p, 1.0f);
+    return fabsf(x) < 0.0625f ? series : hw_exp2(x);
+}
+
+// The step decay for the storage type: fp32 inputs are held to a 1e-4
+// relative tolerance, which needs exp2_decay_accurate; bf16 inputs (5e-3) use
+// the hardware exp2 directly.
+__device__ __forceinline__ float exp2_decay(float x, const float *) { return exp2_decay_accurate(x); }
+__device__ __forceinline__ float exp2_decay(float x, const uint16_t *) { return hw_exp2(x); }
+
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
 // log1p(w) for w in (0, 1]: s = fl(1 + w) loses the low bits of w, so the
 // rounding error c = w - (s - 1) (exact, Fast2Sum) is added back:

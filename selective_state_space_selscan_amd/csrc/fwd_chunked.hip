@@ -109,7 +109,7 @@ __device__ __forceinline__ void phase_a(const TIO *u, const TIO *delta, const TI
         float dt = SOFTPLUS ? softplus(x) : x;
         dt = i < rows ? dt : 0.0f;   // padding steps are the identity (1, 0)
         du[i] = dt * uv[i];
-        rr[i] = pow_path ? hw_exp2(dt * A2_0) : dt * kLog2e;
+        rr[i] = pow_path ? exp2_decay(dt * A2_0, (const TIO *)nullptr) : dt * kLog2e;
         sdelta += dt;
         if (!SUMMARY)
             yv[i] = Dd * uv[i];
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kLanes * W) void fwd_chunked_kernel(
                 const float an = A[d * N + n];
 #pragma unroll
                 for (int i = 0; i < T; ++i)
-                    pw[i] = hw_exp2(rr[i] * an);
+                    pw[i] = exp2_decay(rr[i] * an, (const TIO *)nullptr);
                 Pseg = hw_exp2(sdelta * kLog2e * an);
             }
             float x = 0.0f;

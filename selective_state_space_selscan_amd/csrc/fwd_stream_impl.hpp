@@ -303,7 +303,7 @@ __device__ __forceinline__ void run_chunk(const Chunk &ch, const TIO *Bm, const 
             dt = valid ? dt : 0.0f;        // padding steps are the identity (1, 0)
         const float du = dt * ut;
         float yv = c.Dd * ut;
-        const float r = POW ? hw_exp2(dt * c.A2_0) : 0.0f;
+        const float r = POW ? exp2_decay(dt * c.A2_0, tag<TIO>()) : 0.0f;
         float pw = 1.0f;
         // exact ZOH with structured A: r^(n+1) - 1 = (r - 1)(1 + r + ... + r^n),
         // so B_bar_n / B_n = em * S_n / (n+1) with em = (r - 1) / A[d,0] and
@@ -322,11 +322,11 @@ __device__ __forceinline__ void run_chunk(const Chunk &ch, const TIO *Bm, const 
                     S += a;
                 } else {
                     const float x2 = dt * A2[n];
-                    a = hw_exp2(x2);
+                    a = exp2_decay(x2, tag<TIO>());
                     bu = zoh_coeff(dt, x2, a, invA[n]) * (ut * row_val<N>(bcur, n));
                 }
             } else {
-                a = POW ? (pw *= r) : hw_exp2(dt * A2[n]);
+                a = POW ? (pw *= r) : exp2_decay(dt * A2[n], tag<TIO>());
                 bu = du * row_val<N>(bcur, n);
             }
             h[n] = fmaf(a, h[n], bu);
@@ -441,7 +441,7 @@ __device__ __forceinline__ void summary_chunk_rev(const ChunkT<TTS> &ch, const C
         const float xr = raw_to_f32(ch.x[i], tag<TIO>()) + c.bias;
         const float dt = step_delta<SOFTPLUS, VAR>(xr, c);
         sdelta += dt;
-        const float r = hw_exp2(dt * c.A2_0);
+        const float r = exp2_decay(dt * c.A2_0, tag<TIO>());
         if constexpr ((VAR & kVarZoh) != 0) {
             // Exact ZOH: the step adds Q^(n+1) g S_n / (n+1) B_t[n], with
             // g = (r - 1) / A[d,0] * u and S_n = 1 + r + ... + r^n.  P_n =

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(
         float acc = 0.0f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            h[m] = fmaf(hw_exp2(dA * a[m]), h[m], du * Bv[k][m]);
+            h[m] = fmaf(exp2_decay(dA * a[m], (const T *)nullptr), h[m], du * Bv[k][m]);
             acc = fmaf(Cv[k][m], h[m], acc);
         }
         // sum C.h over the R lanes of the row (all lanes take part)
