@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 6
+#define SELSCAN_ABI_VERSION 7
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -106,8 +106,10 @@ enum selscan_status {
     SELSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
     SELSCAN_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer        */
     SELSCAN_ERR_HIP = 7,         /* a HIP runtime call failed                        */
-    SELSCAN_ERR_TIMEOUT = 8      /* selscan_fwd_status: a bounded wait in a kernel
+    SELSCAN_ERR_TIMEOUT = 8,     /* selscan_fwd_status: a bounded wait in a kernel
                                     gave up, the outputs of that call are invalid    */
+    SELSCAN_ERR_TOO_LARGE = 9    /* selscan_fwd_noalloc: the shape needs more than
+                                    SELSCAN_NOALLOC_SCRATCH_BYTES of workspace       */
 };
 
 /* SELSCAN_ABI_VERSION of the built library. */
@@ -177,6 +179,38 @@ int selscan_fwd(const void *u, const void *delta, const float *A,
                 const float *h0, void *y, float *h_last,
                 int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * forward of selscan_fwd without a workspace argument.  Its workspace is a
+ * fixed device array inside the library, SELSCAN_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) on every device the library runs on, held until the process
+ * ends.  The call allocates and frees nothing: on its first call on a device
+ * it looks up that device's copy of the array (hipGetSymbolAddress, with
+ * that device current), later calls reuse the address.
+ *
+ * Arguments, results and errors as selscan_fwd (the same kernels and plan,
+ * so the same y and h_last bit for bit), without workspace and
+ * workspace_bytes, plus SELSCAN_ERR_TOO_LARGE when
+ * selscan_fwd_workspace_bytes(batch, L, dim, N, dtype) exceeds
+ * SELSCAN_NOALLOC_SCRATCH_BYTES (the workloads here need at most about
+ * 83 MiB at N = 16: batch 16 x L 2048 x dim 5120, or L 131072 x dim 2048),
+ * detected on the host before any HIP call.  The array needs no clearing
+ * between calls (every call writes what it later reads).
+ *
+ * All calls on one device share that device's array: two calls that may
+ * overlap in time on one device (different streams, or host threads with
+ * no ordering between their streams) race on it and may return wrong
+ * results.  Calls on one stream are ordered and safe.
+ */
+#define SELSCAN_NOALLOC_SCRATCH_BYTES (128u << 20)
+int selscan_fwd_noalloc(const void *u, const void *delta, const float *A,
+                        const void *Bm, const void *Cm, const float *D_skip,
+                        const void *z, const float *delta_bias, int delta_softplus,
+                        const float *h0, void *y, float *h_last,
+                        int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
+                        void *stream);
 
 /* Flags of selscan_fwd_ex. */
 #define SELSCAN_FLAG_ZOH_EXACT 1   /* B_bar = (exp(Delta A) - 1) / A * B, Delta B where A = 0 */

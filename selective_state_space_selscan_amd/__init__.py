@@ -29,6 +29,7 @@ from ._abi import (  # noqa: F401
     selscan_bwd_workspace_bytes,
     selscan_fwd,
     selscan_fwd_ex,
+    selscan_fwd_noalloc,
     selscan_fwd_status,
     selscan_fwd_workspace_bytes,
     selscan_state_update,

@@ -57,6 +57,9 @@ def lib():
         L.selscan_supports_n.argtypes = [I64]
         L.selscan_fwd_status.restype = I
         L.selscan_fwd_status.argtypes = [P, P]
+        L.selscan_fwd_noalloc.restype = I
+        L.selscan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64,
+                                          I64, I, P]
         L.selscan_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
         L.selscan_fwd.restype = I
@@ -146,6 +149,42 @@ def selscan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch
     Returns y, or (y, h_last) when ``return_last_state``."""
     return _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0,
                 return_last_state, y, h_last, workspace, stream, None)
+
+
+def selscan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                        Bm: torch.Tensor, Cm: torch.Tensor, y: torch.Tensor,
+                        D_skip: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                        delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
+                        h0: Optional[torch.Tensor] = None, h_last: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None) -> None:
+    """``selscan_fwd`` through ``selscan_fwd_noalloc``: the library's fixed
+    device scratch is the workspace, and the caller provides y (and h_last)
+    as well as the inputs, so the call allocates nothing.  Inputs must
+    already be dense, 16-byte aligned and of the right dtypes (no copies are
+    made here)."""
+    L_ = lib()
+    dev = u.device
+    dt = u.dtype
+    code = _dtype_code(u)
+    batch, L, dim = u.shape
+    N = A.shape[-1]
+    ins = dict(u=(u, dt, (batch, L, dim)), delta=(delta, dt, (batch, L, dim)),
+               A=(A, torch.float32, (dim, N)), Bm=(Bm, dt, (batch, L, N)),
+               Cm=(Cm, dt, (batch, L, N)), D_skip=(D_skip, torch.float32, (dim,)),
+               z=(z, dt, (batch, L, dim)), delta_bias=(delta_bias, torch.float32, (dim,)),
+               h0=(h0, torch.float32, (batch, dim, N)))
+    for name, (t, tdt, shape) in ins.items():
+        if t is not None:
+            _check_out(t, tdt, dev, name, shape)
+    _check_out(y, dt, dev, "y", (batch, L, dim))
+    if h_last is not None:
+        _check_out(h_last, torch.float32, dev, "h_last", (batch, dim, N))
+    rc = L_.selscan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip),
+                                _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                _ptr(y), _ptr(h_last), batch, L, dim, N, code,
+                                _stream(dev, stream))
+    if rc != 0:
+        raise SelscanError(rc, "selscan_fwd_noalloc", L_.selscan_last_hip_error())
 
 
 def selscan_fwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,

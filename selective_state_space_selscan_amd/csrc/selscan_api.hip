@@ -7,6 +7,7 @@
 #include "../../include/selscan.h"
 #include "kernels.hpp"
 
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -108,12 +109,49 @@ int finish_launch(hipError_t e)
 
 namespace {
 
-// Shared by selscan_fwd (ext == NULL) and selscan_fwd_ex.
+// The fixed device scratch of selscan_fwd_noalloc: its workspace, on every
+// device the library runs on, for the life of the process.  Host code never
+// uses the array's name as an address (on the host it is a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[SELSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there).  Returns the hipError_t of the lookup.
+hipError_t scratch_ptr(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Shared by selscan_fwd (ext == NULL), selscan_fwd_ex and (use_scratch)
+// selscan_fwd_noalloc, whose workspace is the device's fixed scratch: there
+// a shape needing more than SELSCAN_NOALLOC_SCRATCH_BYTES is refused, and
+// the scratch is looked up only after every argument check has passed.
 int fwd_common(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
                const float *D_skip, const void *z, const float *delta_bias, int delta_softplus,
                const float *h0, void *y, float *h_last, int64_t batch, int64_t L, int64_t dim,
                int64_t N, int dtype, const selscan::FwdExt *ext, void *workspace,
-               size_t workspace_bytes, void *stream)
+               size_t workspace_bytes, void *stream, bool use_scratch = false)
 {
     if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
         return SELSCAN_ERR_DTYPE;
@@ -137,8 +175,14 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
         if (p && !aligned16(p))
             return SELSCAN_ERR_UNSUPPORTED;
     const size_t need = selscan_fwd_workspace_bytes(batch, L, dim, N, dtype);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (use_scratch) {
+        if (need > (size_t)SELSCAN_NOALLOC_SCRATCH_BYTES)
+            return SELSCAN_ERR_TOO_LARGE;
+        workspace = nullptr;   // the scratch, looked up below: nothing of the caller's
+        workspace_bytes = 0;
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
         return SELSCAN_ERR_WORKSPACE;
+    }
 
     const int64_t es = dtype == SELSCAN_BF16 ? 2 : 4;
     const Range ins[] = {{u, elems * es},     {delta, elems * es},     {A, dim * N * 4},
@@ -153,6 +197,14 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
                 return SELSCAN_ERR_ALIAS;
     if (overlaps(outs[0], outs[1]))
         return SELSCAN_ERR_ALIAS;
+
+    if (use_scratch) {
+        // every argument check has passed: the first HIP call
+        const hipError_t e = scratch_ptr(&workspace);
+        if (e != hipSuccess)
+            return finish_launch(e);
+        workspace_bytes = SELSCAN_NOALLOC_SCRATCH_BYTES;
+    }
 
     selscan::FwdArgs a;
     a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
@@ -262,6 +314,8 @@ const char *selscan_status_string(int status)
     case SELSCAN_ERR_ALIAS: return "an output overlaps an input";
     case SELSCAN_ERR_HIP: return "a HIP runtime call failed";
     case SELSCAN_ERR_TIMEOUT: return "a bounded wait inside a kernel gave up; outputs are invalid";
+    case SELSCAN_ERR_TOO_LARGE:
+        return "the shape needs more workspace than the fixed scratch of selscan_fwd_noalloc";
     default: return "unknown status";
     }
 }
@@ -309,6 +363,16 @@ int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm
 {
     return fwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, y, h_last,
                       batch, L, dim, N, dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+int selscan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *Bm,
+                        const void *Cm, const float *D_skip, const void *z,
+                        const float *delta_bias, int delta_softplus, const float *h0, void *y,
+                        float *h_last, int64_t batch, int64_t L, int64_t dim, int64_t N,
+                        int dtype, void *stream)
+{
+    return fwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, y, h_last,
+                      batch, L, dim, N, dtype, nullptr, nullptr, 0, stream, true);
 }
 
 int selscan_fwd_ex(const void *u, const void *delta, const float *A, const void *Bm,

@@ -26,7 +26,8 @@ no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer tests run 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "selscan.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_WS, ERR_ALIAS, ERR_HIP, ERR_TIMEOUT = range(9)
+(OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_WS, ERR_ALIAS, ERR_HIP, ERR_TIMEOUT,
+ ERR_TOO_LARGE) = range(10)
 
 
 def header_functions():
@@ -52,7 +53,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_supported_n():
     L = ss.lib()
-    for s in range(9):
+    for s in range(10):
         assert len(L.selscan_status_string(s)) > 0
         assert L.selscan_status_string(s) != b"unknown status"
     assert L.selscan_status_string(99) == b"unknown status"
@@ -362,3 +363,48 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_abi, "_LIB_PATH", "/nonexistent/libselscan.so")
     with pytest.raises(RuntimeError, match="not built"):
         _abi.lib()
+
+
+def noalloc_args(**kw):
+    a = fwd_args(**kw)
+    return a[:17] + [a[19]]   # no workspace, workspace_bytes
+
+
+INVALID_NOALLOC = [
+    # 64 x 4096 x 4096 at N = 64 needs about 1.2 GB of workspace, more than the
+    # 128 MiB fixed scratch
+    ("beyond_scratch", dict(batch=64, L=4096, dim=4096, N=64), ERR_TOO_LARGE),
+    ("dtype", dict(dtype=2), ERR_DTYPE),
+    ("L0", dict(L=0), ERR_SHAPE),
+    ("u_null", dict(u=None), ERR_NULL),
+    ("N5", dict(N=5), ERR_UNSUP),
+    ("misaligned_u", dict(u=ctypes.c_void_p(BASE + STEP + 2)), ERR_UNSUP),
+    ("y_aliases_u", dict(y=ctypes.c_void_p(BASE + STEP + 64)), ERR_ALIAS),
+]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("name,kw,status", INVALID_NOALLOC, ids=[c[0] for c in INVALID_NOALLOC])
+def test_fwd_noalloc_rejects_invalid_arguments(name, kw, status):
+    """Checked on the host before any HIP call, like selscan_fwd, and shapes
+    whose workspace exceeds the fixed scratch are refused."""
+    L = ss.lib()
+    assert L.selscan_fwd_workspace_bytes(64, 4096, 4096, 64, 1) > header_constant_expr(
+        "SELSCAN_NOALLOC_SCRATCH_BYTES")
+    assert L.selscan_fwd_noalloc(*noalloc_args(**kw)) == status
+    assert L.selscan_last_hip_error() == 0
+
+
+def header_constant_expr(name):
+    m = re.search(r"#define\s+%s\s+\((\d+)u\s*<<\s*(\d+)\)" % name, open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_scratch_holds_the_workloads():
+    """The fixed scratch holds the forward workspace of every workload here."""
+    L = ss.lib()
+    limit = header_constant_expr("SELSCAN_NOALLOC_SCRATCH_BYTES")
+    assert limit == 128 << 20
+    for shape in ((1, 256, 64), (8, 2048, 1536), (1, 131072, 2048), (16, 2048, 5120)):
+        need = L.selscan_fwd_workspace_bytes(*shape, 16, 1)
+        assert 0 < need <= limit, (shape, need)
