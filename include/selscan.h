@@ -374,7 +374,9 @@ int selscan_bwd_ex(const void *u, const void *delta, const float *A,
  *   z          (batch, dim)     dtype   NULL means no gate
  *   y          (batch, dim)     dtype   output, written
  *
- * Required: batch, dim >= 1; N supported; state, u, delta, A, Bm, Cm, y non-NULL.
+ * Required: batch, dim >= 1; N supported; batch * dim * N < 2^31 (the state
+ * is indexed with 32 bits: SELSCAN_ERR_UNSUPPORTED beyond); state, u, delta,
+ * A, Bm, Cm, y non-NULL.
  */
 int selscan_state_update(float *state, const void *u, const void *delta, const float *A,
                          const void *Bm, const void *Cm, const float *D_skip,

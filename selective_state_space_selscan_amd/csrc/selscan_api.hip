@@ -468,7 +468,8 @@ int selscan_state_update(float *state, const void *u, const void *delta, const f
         return SELSCAN_ERR_SHAPE;
     if (!state || !u || !delta || !A || !Bm || !Cm || !y)
         return SELSCAN_ERR_NULL;
-    if (!supported_n(N))
+    // 32-bit state indices in the kernel: batch * dim * N < 2^31
+    if (!supported_n(N) || states >= ((int64_t)1 << 31))
         return SELSCAN_ERR_UNSUPPORTED;
     const void *all[] = {state, u, delta, A, Bm, Cm, D_skip, z, delta_bias, y};
     for (const void *p : all)

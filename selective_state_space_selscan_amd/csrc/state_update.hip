@@ -22,8 +22,11 @@ namespace {
 
 constexpr int kBlock = 256;
 // Rows per lane, loads of all of them issued first: 2 puts two state loads
-// in flight per lane (cold step 41.1 -> 38.4 us on batch 256, D 5120, N 16;
-// 4 was slower, 48 us).
+// in flight per lane.  Measured on batch 256, D 5120, N 16 (cold step, the
+// state from HBM): 35.4 us at 2 rows per lane, 37.8 at 1, 38.1 at 4; one
+// lane per row (all 16 states in a lane, its loads 64 B apart across the
+// wave) 44.7; a persistent grid loading the next chunk while updating the
+// current one 39-45; non-temporal state loads and stores 36.5.
 constexpr int kStateRowsPerLane = 2;
 
 template <typename T>
@@ -51,27 +54,34 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(
     float *__restrict__ state, const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ A, const T *__restrict__ Bm, const T *__restrict__ Cm,
     const float *__restrict__ D_skip, const T *__restrict__ z,
-    const float *__restrict__ delta_bias, int delta_softplus, T *__restrict__ y, int64_t dim,
-    int64_t rows)
+    const float *__restrict__ delta_bias, int delta_softplus, T *__restrict__ y, uint32_t dim,
+    double inv_dim, uint32_t rows)
 {
     static_assert(N % 4 == 0 && kBlock % (N / 4) == 0, "N/4 lanes per row");
-    constexpr int R = N / 4;                       // lanes per (b, d) row
-    constexpr int64_t kRowsPerSlot = kBlock / R;   // rows one slot of the block covers
+    constexpr uint32_t R = N / 4;                       // lanes per (b, d) row
+    constexpr uint32_t kRowsPerSlot = kBlock / R;       // rows one slot of the block covers
     // K slots per lane: the block covers K * kRowsPerSlot consecutive rows, slot
     // k the k-th run of kRowsPerSlot.  All K rows' loads are issued before any
     // row is computed and stored, so each lane has K state loads in flight.
-    const int q = (int)(threadIdx.x % R);          // this lane's float4 of a row
-    const int64_t row0 = (int64_t)blockIdx.x * (K * kRowsPerSlot) + threadIdx.x / R;
+    // Indices are 32-bit (rows * N < 2^31 is checked on the host); b = row /
+    // dim comes from a double-precision reciprocal, exact after one
+    // correction step for row < 2^31.
+    const uint32_t q = threadIdx.x % R;                 // this lane's float4 of a row
+    const uint32_t row0 = blockIdx.x * (K * kRowsPerSlot) + threadIdx.x / R;
     float4 h4[K], a4[K];
-    float Bv[K][4], Cv[K][4], ut[K], xr[K], zt[K];
-    int64_t r[K];
+    float Bv[K][4], Cv[K][4], ut[K], xr[K], zt[K], Dd[K];
+    uint32_t r[K];
     bool valid[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int64_t row = row0 + k * kRowsPerSlot;
+        const uint32_t row = row0 + k * kRowsPerSlot;
         valid[k] = row < rows;
         r[k] = valid[k] ? row : rows - 1;          // tail lanes compute on a valid row
-        const int64_t b = r[k] / dim, d = r[k] - (r[k] / dim) * dim;
+        uint32_t b = (uint32_t)((double)r[k] * inv_dim);
+        int64_t dd = (int64_t)r[k] - (int64_t)b * dim;
+        if (dd < 0) { --b; dd += dim; }
+        if (dd >= (int64_t)dim) { ++b; dd -= dim; }
+        const uint32_t d = (uint32_t)dd;
         h4[k] = *(reinterpret_cast<const float4 *>(state + r[k] * N) + q);
         a4[k] = *reinterpret_cast<const float4 *>(A + d * N + 4 * q);
         load4<T>(Bm + b * N + 4 * q, Bv[k]);
@@ -79,10 +89,10 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(
         ut[k] = load_elem(u, r[k]);
         xr[k] = load_elem(delta, r[k]) + (delta_bias ? delta_bias[d] : 0.0f);
         zt[k] = z ? load_elem(z, r[k]) : 0.0f;
+        Dd[k] = D_skip ? D_skip[d] : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int64_t d = r[k] - (r[k] / dim) * dim;
         const float dt = delta_softplus ? softplus(xr[k]) : xr[k];
         const float du = dt * ut[k];
         const float dA = dt * kLog2e;
@@ -96,12 +106,12 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(
         }
         // sum C.h over the R lanes of the row (all lanes take part)
 #pragma unroll
-        for (int off = R / 2; off > 0; off >>= 1)
+        for (uint32_t off = R / 2; off > 0; off >>= 1)
             acc += __shfl_xor(acc, off, R);
         if (valid[k]) {
             *(reinterpret_cast<float4 *>(state + r[k] * N) + q) = make_float4(h[0], h[1], h[2], h[3]);
             if (q == 0) {
-                float yv = fmaf(D_skip ? D_skip[d] : 0.0f, ut[k], acc);
+                float yv = fmaf(Dd[k], ut[k], acc);
                 if (z)
                     yv *= silu(zt[k]);
                 store_elem(y, r[k], yv);
@@ -114,15 +124,16 @@ template <int N, typename T>
 hipError_t launch_typed(const StepArgs &a, hipStream_t stream)
 {
     const int64_t rows = a.batch * a.dim;
+    if (rows * a.N >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;   // refused on the host before this point
     constexpr int64_t rows_per_block = kStateRowsPerLane * (kBlock / (N / 4));
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-    if (blocks > 0x7fffffff)
-        return hipErrorInvalidValue;
     hipLaunchKernelGGL((state_update_kernel<N, T, kStateRowsPerLane>), dim3((unsigned)blocks),
                        dim3(kBlock), 0,
                        stream, a.state, (const T *)a.u, (const T *)a.delta, a.A,
                        (const T *)a.Bm, (const T *)a.Cm, a.D_skip, (const T *)a.z, a.delta_bias,
-                       a.delta_softplus, (T *)a.y, a.dim, rows);
+                       a.delta_softplus, (T *)a.y, (uint32_t)a.dim, 1.0 / (double)a.dim,
+                       (uint32_t)rows);
     return hipGetLastError();
 }
 

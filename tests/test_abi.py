@@ -347,6 +347,8 @@ INVALID_STEP = [
     ("misaligned_state", dict(state=ctypes.c_void_p(BASE + STEP + 4)), ERR_UNSUP),
     ("y_aliases_state", dict(y=ctypes.c_void_p(BASE + STEP + 4096)), ERR_ALIAS),
     ("state_aliases_u", dict(u=ctypes.c_void_p(BASE + STEP + 256)), ERR_ALIAS),
+    # the state is indexed with 32 bits: batch * dim * N < 2^31
+    ("state_too_large", dict(batch=1 << 15, dim=1 << 12, N=16), ERR_UNSUP),
 ]
 
 
