@@ -163,9 +163,10 @@ def make_inputs(w, dev, rotate):
     return inp, sets
 
 
-def pmc_run(w, reps=3):
+def pmc_run(w, reps=3, warmup=200):
     """Workload for the counter runs: one plain 1 GiB device copy (the
-    calibration), then ``reps`` forward calls."""
+    calibration), ``warmup`` forward calls (the clocks ramp up), then ``reps``
+    forward calls, the ones the counters are read on."""
     import torch
 
     import selective_state_space_selscan_amd as ss
@@ -178,11 +179,11 @@ def pmc_run(w, reps=3):
     del src, dst
     _, sets = make_inputs(w, dev, 1)
     t = sets[0]
-    for _ in range(reps):
+    for _ in range(warmup + reps):
         ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
                        t["delta_bias"], True, None, return_last_state=w.want_last_state)
     torch.cuda.synchronize()
-    print("pmc-run done", w.name, reps, flush=True)
+    print("pmc-run done", w.name, warmup, reps, flush=True)
 
 
 def parse_pmc(w, fetch_dir, write_dir, reps=3):
@@ -205,6 +206,8 @@ def parse_pmc(w, fetch_dir, write_dir, reps=3):
         # the calibration copy is the largest copyBuffer dispatch (1 GiB)
         copy = sorted((v for (i, k), v in rows if "copyBuffer" in k), reverse=True)
         scan = [(k, v) for (i, k), v in rows if "selscan" in k]
+        # the last reps calls (after the warmup calls): reps x the kernels of a call
+        scan = scan[-reps * len({k for k, _ in scan}):]
         factor = COPY_CAL_BYTES / (copy[0] * 1024.0) if copy and copy[0] > 0 else None
         kib_per_call = sum(v for _, v in scan) / reps
         out[name] = {"counter": counter, "kib_per_call_raw": kib_per_call,
@@ -363,16 +366,27 @@ def device_copy_gbps(dev, nbytes=1 << 29, reps=10):
     return 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
 
 
-def bwd_valu_slots(N, gate, es):
-    """fp32 VALU slots per (b, l, d) element of the backward as built: the
-    chunk's states recomputed from a checkpoint (3 N: A_bar, Delta u B, FMA),
-    the adjoint step (11 N: lambda, readout, A_bar h_{t-1}, its product with
-    lambda, the dDelta and dA sums, lambda.B, the dB and dC terms, A_bar,
-    the carry) and about 60 per element (softplus and sigmoid twice, SiLU and
-    its derivative, widening, the per-element gradients).  The checkpoint
-    and summary passes and the LDS reductions are extra work of the
-    recomputation scheme, not counted."""
-    return 14 * N + 60
+def bwd_valu_slots(N, gate, es, flags=0, conv_k=0):
+    """fp32 VALU slots per (b, l, d) element of the backward as built, counted
+    from the inner loops of its main pass (the summary and checkpoint passes
+    and the carries are extra work of the recomputation scheme, not counted;
+    a transcendental counts two slots).  Per state n:
+      Euler B_bar (plain, reverse):   recompute 3 (A_bar by the power chain,
+        Delta u B, state FMA); adjoint step 11 (lambda, readout, A_bar h_{t-1},
+        its product with lambda, the dDelta and dA sums, lambda.B, the dB and
+        dC terms, A_bar, the carry); the LDS sums of dB and dC 2  -> 16 N
+      exact ZOH: recompute 14 (the coefficient (e - 1)/A with its series
+        branch: 9, times u B: 2); adjoint 40 (the coefficient again, its
+        derivative in A with its series branch: 13, and the extra terms of
+        dDelta and dA); the LDS sums 2                            -> 56 N
+    Per element about 60 (softplus and sigmoid twice, SiLU and its derivative,
+    widening, the per-element gradients and stores); the conv prologue adds
+    48 (the conv and SiLU of the scan input recomputed in the main, summary
+    and checkpoint passes, 10 each, and in the main pass the conv's own
+    backward: SiLU' of the pre-activation, the dconv_w and dconv_b sums and
+    the transposed conv of dx, 18)."""
+    per_n = 56 if flags & VARIANT_FLAGS["zoh"] else 16
+    return per_n * N + 60 + (48 if conv_k else 0)
 
 
 def bench_bwd(w, args):
@@ -426,8 +440,8 @@ def bench_bwd(w, args):
     wall, call_mean, call_ms, quarters = timed_steps(step, args.steps, args.warmup, stream)
     es = 2 if w.dtype == si.BF16 else 4
     elems = w.batch * w.L * w.dim
-    slots_el = bwd_valu_slots(w.N, w.gate, es) + (algorithmic_valu_slots(w.N, w.gate, es)
-                                                   if pair else 0)
+    slots_el = bwd_valu_slots(w.N, w.gate, es, vflags, vconv) + (
+        algorithmic_valu_slots(w.N, w.gate, es) if pair else 0)
     slots = slots_el * elems
     # bytes the backward must move: the forward's inputs once, dy, and the
     # gradients du, ddelta, dz (dtype) and dB, dC (fp32) once
@@ -459,8 +473,7 @@ def bench_bwd(w, args):
     if args.variant:
         res["variant"] = args.variant
         if not pair:
-            res["roofline"]["kernel"] = "selscan_bwd_ex call (%s); slots of the default path" \
-                % args.variant
+            res["roofline"]["kernel"] = "selscan_bwd_ex call (%s, all passes)" % args.variant
     print(json.dumps(res), flush=True)
 
 

@@ -30,5 +30,13 @@ def test_valu_slot_counts():
     assert bench.algorithmic_valu_slots(16, True, 2) == 87
     assert bench.algorithmic_valu_slots(16, True, 2) - bench.algorithmic_valu_slots(8, True, 2) \
         == 4 * 8
-    # backward estimate: 14 N + 60
-    assert bench.bwd_valu_slots(16, True, 2) == 284
+    # general A: an exp2 (3 slots) per state for the power chain's multiply,
+    # and no exp of Delta A[d,0]: 6 N + 20
+    assert bench.algorithmic_valu_slots(16, True, 2, general_a=True) == 116
+    # backward, counted per variant: 16 N + 60 (Euler), 56 N + 60 (exact ZOH),
+    # and 48 more per element with the conv prologue
+    assert bench.bwd_valu_slots(16, True, 2) == 316
+    assert bench.bwd_valu_slots(16, True, 2, flags=2) == 316
+    assert bench.bwd_valu_slots(16, True, 2, flags=1) == 956
+    assert bench.bwd_valu_slots(16, True, 2, flags=0, conv_k=4) == 364
+    assert bench.bwd_valu_slots(16, True, 2, flags=3, conv_k=4) == 1004
