@@ -477,6 +477,58 @@ def bench_bwd(w, args):
     print(json.dumps(res), flush=True)
 
 
+def torch_loop_context(w, calls=2):
+    """Context, not the product: the selective scan written as a plain PyTorch
+    loop over timesteps on the GPU, the way the Mamba tutorial's section 4.2
+    listing writes it (per step: A_bar = exp(Delta A), h = A_bar h + Delta B u,
+    y = C.h, all as tensor ops; then D u and the SiLU(z) gate), in fp32, on
+    the same inputs.  Returns the mean wall time per call and the ratio to
+    selscan_fwd, which the pages' 20-40x claim is about."""
+    import torch
+    import torch.nn.functional as F
+
+    import selective_state_space_selscan_amd as ss
+    dev = torch.device("cuda:0")
+    _, sets = make_inputs(w, dev, 1)
+    t = sets[0]
+    u, dl, z = (t[k].float() for k in ("u", "delta", "z"))
+    Bm, Cm = t["Bm"].float(), t["Cm"].float()
+    A, D, bias = t["A"], t["D_skip"], t["delta_bias"]
+
+    def loop():
+        dt = F.softplus(dl + bias)
+        h = torch.zeros((w.batch, w.dim, w.N), dtype=torch.float32, device=dev)
+        ys = []
+        for s in range(w.L):
+            dA = torch.exp(dt[:, s, :, None] * A)
+            h = dA * h + (dt[:, s, :, None] * u[:, s, :, None]) * Bm[:, s, None, :]
+            ys.append((h * Cm[:, s, None, :]).sum(-1))
+        y = torch.stack(ys, 1) + D * u
+        return y * F.silu(z)
+
+    loop()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        loop()
+    torch.cuda.synchronize()
+    loop_ms = 1e3 * (time.perf_counter() - t0) / calls
+    for _ in range(20):
+        ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                       t["delta_bias"], True, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(50):
+        ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                       t["delta_bias"], True, None)
+    torch.cuda.synchronize()
+    fwd_ms = 1e3 * (time.perf_counter() - t0) / 50
+    return {"torch_loop_ms_per_call": loop_ms, "selscan_fwd_ms_per_call": fwd_ms,
+            "speedup": loop_ms / fwd_ms, "calls": calls,
+            "what": "plain PyTorch loop over the L timesteps on the GPU (fp32 tensor ops per "
+                    "step), same inputs; context for the pages' 20-40x claim"}
+
+
 VARIANT_FLAGS = {"zoh": 1, "rev": 2}
 
 
@@ -504,6 +556,9 @@ def main():
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fwdbwd"), default="fwd")
+    ap.add_argument("--torch-loop", action="store_true",
+                    help="context only: time a plain PyTorch loop over timesteps against "
+                         "selscan_fwd on the workload, print one JSON line")
     ap.add_argument("--variant", default="", help="variants: zoh, rev, convK (fwd or bwd)")
     ap.add_argument("--a", dest="a_form", choices=("s4d", "general"), default="s4d",
                     help="A = -(n+1) (S4D-real: the power-chain A_bar) or a perturbed, "
@@ -524,6 +579,9 @@ def main():
         return
     if args.pmc_run:
         pmc_run(w)
+        return
+    if args.torch_loop:
+        print(json.dumps({"workload": w.name, **torch_loop_context(w)}), flush=True)
         return
     if args.which in ("bwd", "fwdbwd"):
         bench_bwd(w, args)
