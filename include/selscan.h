@@ -265,8 +265,11 @@ int selscan_fwd_ex(const void *u, const void *delta, const float *A,
  * valid shape; 0 for invalid arguments).  It holds the part summaries of the
  * forward and of the adjoint, the recomputation checkpoints (the state at the
  * start of every 4-step chunk: batch * ceil(dim/64) * ceil(L/4) * N * 256
- * bytes) and the partial sums of the reduced gradients.  No initialisation.
- * The same size serves selscan_bwd_ex, with or without the conv prologue.
+ * bytes), the partial sums of the reduced gradients and, for the conv
+ * prologue of selscan_bwd_ex, its output and that output's gradient (fp32,
+ * batch * L * dim * 4 bytes, counted for every call: the size takes no
+ * flags).  No initialisation.  The same size serves selscan_bwd_ex, with or
+ * without the conv prologue.
  */
 size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype);
 

@@ -138,8 +138,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N)
     w.pbias = off; off = align256(off + slots * dim * 4);
     w.pW = off; off = align256(off + slots * dim * kMaxConv * 4);
     w.pWb = off; off = align256(off + slots * dim * 4);
-    w.xown = off; off = align256(off + (size_t)w.p.groups * w.p.parts * kHalo * kLanes * 4);
-    w.xcarry = off; off = align256(off + (size_t)w.p.groups * w.p.parts * kHalo * kLanes * 4);
+    // the conv prologue's scan inputs and their gradients (fp32); every
+    // variant shares one size query, so the buffer is always counted
+    w.uconv = off; off = align256(off + (size_t)batch * L * dim * 4);
     w.total = off + 256;   // room to align the base
     return w;
 }

@@ -49,11 +49,15 @@
 //     gu_s the gradient of u_s and gp_s = gu_s SiLU'(p_s):
 //       dx_{s'} = sum_m w_m gp_{s'+3-m},  dw_m = sum_s gp_s x_{s-3+m},
 //       db = sum_s gp_s.
-//     dx_s needs gp of the steps s..s+3: the wave keeps the contributions of
-//     the three later steps in a register ring.  For the last three steps of
-//     a part (but the last), the later steps belong to the next part's wave:
-//     both partial sums go to the workspace and a fix-up pass adds them.
+//     The checkpoint pass, which forms u_s anyway, stores it (fp32) in the
+//     workspace; the main pass reads it there (kVarUf: no conv taps, window
+//     or ring in its registers, so it keeps the plain pass's occupancy) and
+//     stores gu_s over it, fp32; an epilogue pass then forms gp, dx and the
+//     per-part sums of dw, db.  Each epilogue wave recomputes gp of the
+//     kHalo steps after its part rather than wait for the next part's wave.
 #pragma once
+
+#include <type_traits>
 
 #include "fwd_stream_impl.hpp"
 
@@ -66,6 +70,7 @@ using stream::kMaxConv;
 using stream::kVarConv;
 using stream::kVarExt;
 using stream::kVarRev;
+using stream::kVarUf;
 using stream::kVarZoh;
 using stream::RowRaw;
 using stream::TT;
@@ -79,7 +84,19 @@ using stream::step_soff;
 
 constexpr int kLdsStride = kLanes + 1;  // padded rows: conflict-free LDS transposes
 constexpr int kHalo = kMaxConv - 1;     // conv window: steps before a step
-static_assert(TT >= kHalo, "the conv window must fit in the chunk before");
+
+// Element type of the main pass's scan input and of its gradient: fp32 in
+// the workspace with kVarUf (the conv prologue's output), else the I/O type.
+template <int VAR, typename TIO>
+using UType = typename std::conditional<(VAR & kVarUf) != 0, float, TIO>::type;
+
+// Scalar step offset into an array of the I/O arrays' rows with elements S
+// times as wide; the out-of-range offset stays out of range.
+template <int S>
+__device__ __forceinline__ int widen_soff(int soff)
+{
+    return (S == 1 || soff == stream::kStoreOffsetOutOfRange) ? soff : soff * S;
+}
 
 // Per-wave setup shared by the backward kernels (the forward kernel's, with
 // the same group/part decomposition).
@@ -167,20 +184,20 @@ __device__ __forceinline__ float zoh_dcoeff(float dt, float x2, float e, float c
     return fabsf(x2) < 0.5f ? series : direct;
 }
 
-// Inputs of TT steps for the backward: u (the raw input x with the conv
-// prologue), Delta_raw, z, dy (raw bits).
+// Inputs of TT steps for the backward: u (the I/O type, or fp32 with
+// kVarUf), Delta_raw, z, dy (raw bits).
 struct BwdChunk {
     uint32_t u[TT], x[TT], z[TT], dy[TT];
 };
 
 // Loads the chunk at scan step t0.  Chunks past the part's end, or starting
-// below `lo` (the part's start, or the chunk before it for the conv window),
-// read nothing (zeros).
-template <int VAR, typename TIO>
-__device__ __forceinline__ void load_bwd_chunk(BwdChunk &ch, const TIO *u, const TIO *delta,
+// below `lo` (the part's start), read nothing (zeros).
+template <int VAR, typename TIO, typename TU>
+__device__ __forceinline__ void load_bwd_chunk(BwdChunk &ch, const TU *u, const TIO *delta,
                                                const TIO *z, const TIO *dy, const WaveCtx &c,
                                                int64_t t0, bool with_u, int64_t lo)
 {
+    constexpr int S = (int)(sizeof(TU) / sizeof(TIO));
     int64_t rows = c.l_end - t0;
     rows = rows < 0 ? 0 : (rows > TT ? TT : rows);
     if (t0 < lo)
@@ -190,14 +207,15 @@ __device__ __forceinline__ void load_bwd_chunk(BwdChunk &ch, const TIO *u, const
     const int64_t safe = rows > 0 ? elem : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(delta + safe, bytes);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(dy + safe, bytes);
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(with_u ? u + safe : nullptr, with_u ? bytes : 0);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(with_u ? u + safe : nullptr,
+                                                with_u ? bytes * S : 0);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(z ? z + safe : nullptr, z ? bytes : 0);
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
         const int soff = step_soff<VAR>(c, i, (int)rows);
         ch.x[i] = buf_load_raw(rx, c.voff, soff, delta);
         ch.dy[i] = buf_load_raw(ry, c.voff, soff, dy);
-        ch.u[i] = buf_load_raw(ru, c.voff, soff, u);
+        ch.u[i] = buf_load_raw(ru, c.voff * S, widen_soff<S>(soff), u);
         ch.z[i] = buf_load_raw(rz, c.voff, soff, z);
     }
 }
@@ -303,14 +321,22 @@ __device__ __forceinline__ void adjoint_summary_wave(
 // ---------------------------------------------------------------------------
 // 3. checkpoints: the state entering every TT-step chunk
 // ---------------------------------------------------------------------------
+// With the conv prologue the walk forms the scan inputs u_s itself, stores
+// them (fp32, same (batch, L, dim) layout as x) to uconv for the main pass,
+// and runs the recurrence on them as fp32 (kVarUf).  voff_u: this lane's
+// byte offset in uconv's rows, out of range for lanes past dim.
 template <int N, bool POW, bool SP, int VAR, typename TIO>
 __device__ __forceinline__ void checkpoint_part(const TIO *__restrict__ u,
                                                 const TIO *__restrict__ delta,
                                                 const TIO *__restrict__ Bm, const WaveCtx &c,
                                                 const float (&A2)[N], const float (&invA)[N],
                                                 float (&h)[N], float *__restrict__ ck,
-                                                float (&win)[kHalo])
+                                                float (&win)[kHalo], float *__restrict__ uconv,
+                                                int voff_u)
 {
+    constexpr bool CONV = (VAR & kVarConv) != 0;
+    constexpr int VW = CONV ? ((VAR & ~kVarConv) | kVarUf) : VAR;
+    constexpr int S = (int)(sizeof(float) / sizeof(TIO));
     float sdelta = 0.0f;
     stream::Chunk A, B;
     int64_t t0 = c.l_begin;
@@ -321,8 +347,22 @@ __device__ __forceinline__ void checkpoint_part(const TIO *__restrict__ u,
 #pragma unroll
         for (int n = 0; n < N; ++n)
             o[n * kLanes] = h[n];
-        stream::run_any_chunk<N, true, false, SP, POW, VAR>(A, Bm, Bm, (TIO *)nullptr, c, t0,
-                                                            A2, invA, h, sdelta, win);
+        if constexpr (CONV) {
+            // steps past the part's end land past the descriptor's range
+            const int rows = (int)(c.l_end - t0 < TT ? c.l_end - t0 : TT);
+            const int64_t elem = (c.bL + stream::run_t_lo<VAR>(c, t0, rows)) * c.dim + c.d0;
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(uconv + elem, (rows * c.dim - c.d0) * (int64_t)sizeof(float));
+#pragma unroll
+            for (int i = 0; i < TT; ++i) {
+                const float us = stream::step_input<VAR, TIO>(A.u[i], c, win);
+                A.u[i] = __float_as_uint(us);
+                buf_store(rs, voff_u, widen_soff<S>(step_soff<VAR>(c, i, rows)), us,
+                          (float *)nullptr);
+            }
+        }
+        stream::run_any_chunk<N, true, false, SP, POW, VW>(A, Bm, Bm, (TIO *)nullptr, c, t0,
+                                                           A2, invA, h, sdelta, win);
         t0 += TT;
         if (t0 >= c.l_end)
             break;
@@ -344,8 +384,9 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_pass23_kernel(
     const TIO *__restrict__ dy, const float *__restrict__ A, const TIO *__restrict__ Bm,
     const TIO *__restrict__ Cm, const float *__restrict__ delta_bias, int delta_softplus,
     const float *__restrict__ h0, const float *__restrict__ fentry, float *__restrict__ asumm,
-    float *__restrict__ ckpt, int64_t nck, ExtParams ext, int64_t L, int64_t dim, int64_t groups,
-    int parts, int64_t part_len, int64_t adj_blocks, int64_t ck_blocks)
+    float *__restrict__ ckpt, float *__restrict__ uconv, int64_t nck, ExtParams ext, int64_t L,
+    int64_t dim, int64_t groups, int parts, int64_t part_len, int64_t adj_blocks,
+    int64_t ck_blocks)
 {
     const int64_t bid = blockIdx.x;
     bool is_adj = ROLES == 1;
@@ -405,15 +446,19 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_pass23_kernel(
                 h[n] = h0 ? h0[(c.b * dim + w.d) * N + n] : 0.0f;
         }
         float *ck = ckpt + w.grp * nck * (N * kLanes) + w.lane;
+        const int vu = w.active ? w.lane * (int)sizeof(float) : stream::kStoreOffsetOutOfRange;
         // with kVarExt the softplus switch is read at run time (SP unused)
         const bool sp = (VAR & kVarExt) != 0 || delta_softplus;
+#define SELSCAN_CKPT(P, SPV)                                                                      \
+    checkpoint_part<N, P, SPV, VAR>(u, delta, Bm, c, A2, invA, h, ck, win, uconv, vu)
         if (pow_path) {
-            if (sp) checkpoint_part<N, true, true, VAR>(u, delta, Bm, c, A2, invA, h, ck, win);
-            else checkpoint_part<N, true, false, VAR>(u, delta, Bm, c, A2, invA, h, ck, win);
+            if (sp) SELSCAN_CKPT(true, true);
+            else SELSCAN_CKPT(true, false);
         } else {
-            if (sp) checkpoint_part<N, false, true, VAR>(u, delta, Bm, c, A2, invA, h, ck, win);
-            else checkpoint_part<N, false, false, VAR>(u, delta, Bm, c, A2, invA, h, ck, win);
+            if (sp) SELSCAN_CKPT(false, true);
+            else SELSCAN_CKPT(false, false);
         }
+#undef SELSCAN_CKPT
     }
 }
 
@@ -421,39 +466,32 @@ __global__ __launch_bounds__(kLanes * 4) void bwd_pass23_kernel(
 // 4. main backward pass
 // ---------------------------------------------------------------------------
 struct BwdOut {
-    void *du, *ddelta, *dz;
+    void *du;           // gradient of the scan input: the I/O type, or fp32 with kVarUf
+    void *ddelta, *dz;
     float *pB, *pC;     // (groups_per_row, batch, L, N) partial sums over 64 channels
     float *pA;          // (batch, parts, dim, N) partial sums over a part
     float *pD, *pbias;  // (batch, parts, dim)
     float *dh0;         // (batch, dim, N) or null
-    // conv prologue only
-    float *pW;          // (batch, parts, dim, conv_k) partial sums of dconv_w
-    float *pWb;         // (batch, parts, dim) partial sums of dconv_b
-    float *xown;        // (groups, parts, kHalo, 64): dx of a part's last kHalo steps, own share
-    float *xcarry;      // (groups, parts, kHalo, 64): a part's share of the kHalo steps before it
 };
 
 // Per-wave running sums of the main pass.
 struct BwdAcc {
     float dD, dbias;
-    float dcw[kMaxConv], dcb;   // conv prologue
-    float ring[kHalo];          // conv: shares of dx of the kHalo steps before the current one
 };
 
 // TT steps: states recomputed from the chunk's checkpoint, then the adjoint
-// steps from the last to the first.  prev: the chunk before (its raw inputs
-// are the conv window; unused without the conv prologue).
+// steps from the last to the first.
 template <int N, bool POW, int VAR, typename TIO>
-__device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &prev, const TIO *Bm,
-                                          const TIO *Cm, const WaveCtx &c, int64_t t0,
-                                          const float *ck, const float (&A2)[N],
-                                          const float (&invA)[N], float (&g)[N], float (&dA)[N],
-                                          BwdAcc &acc, bool gated, const BwdOut &o,
-                                          int64_t grp_in_row, int64_t batch, float *lds, int lane,
-                                          bool active, float *xown)
+__device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, const TIO *Cm,
+                                          const WaveCtx &c, int64_t t0, const float *ck,
+                                          const float (&A2)[N], const float (&invA)[N],
+                                          float (&g)[N], float (&dA)[N], BwdAcc &acc, bool gated,
+                                          const BwdOut &o, int64_t grp_in_row, int64_t batch,
+                                          float *lds, int lane, bool active)
 {
     constexpr bool ZOH = (VAR & kVarZoh) != 0;
-    constexpr bool CONV = (VAR & kVarConv) != 0;
+    using TU = UType<VAR, TIO>;
+    constexpr int S = (int)(sizeof(TU) / sizeof(TIO));
     // Two equivalent forms of the per-step addressing and ordering, each the
     // faster one (fewer scalar-register spills, measured) for its case: with
     // the direction fixed at compile time, rows and inputs are formed at use;
@@ -472,30 +510,11 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
             return valid ? row0 + i * dir : row0;
         }
     };
-    // scan inputs of the TT steps; with the conv prologue, the raw inputs of
-    // steps t0-kHalo .. t0+TT-1 (xw[j] is step t0-kHalo+j) and the
-    // pre-activations
-    float xw[kHalo + TT], us[TT], pre[TT];
-#pragma unroll
-    for (int j = 0; j < kHalo; ++j)
-        xw[j] = CONV ? raw_f<TIO>(prev.u[TT - kHalo + j]) : 0.0f;
+    // scan inputs of the TT steps
+    float us[TT];
 #pragma unroll
     for (int i = 0; i < TT; ++i)
-        xw[kHalo + i] = raw_f<TIO>(ch.u[i]);
-#pragma unroll
-    for (int i = 0; i < TT; ++i) {
-        if constexpr (CONV) {
-            float a = c.cb;
-#pragma unroll
-            for (int m = 0; m < kMaxConv; ++m)
-                a = fmaf(c.cw[m], xw[i + m], a);
-            pre[i] = a;
-            us[i] = silu(a);
-        } else {
-            pre[i] = 0.0f;
-            us[i] = xw[kHalo + i];
-        }
-    }
+        us[i] = raw_f<TU>(ch.u[i]);
     // recompute h_t for the TT steps
     float hs[TT][N];
     {
@@ -507,7 +526,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
         for (int i = 0; i < TT; ++i) {
             RowRaw<N, TIO> brow;
             fetch_row(brow, Bm, step_row(i, i < rows));
-            const float ut = (FIXED && !CONV) ? raw_f<TIO>(ch.u[i]) : us[i];
+            const float ut = FIXED ? raw_f<TU>(ch.u[i]) : us[i];
             const float xr = raw_f<TIO>(ch.x[i]) + c.bias;
             const float sp = softplus(xr);
             float dt = c.softplus ? sp : xr;
@@ -530,10 +549,11 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
     // adjoint steps
     const int64_t elem = (c.bL + run_t_lo<VAR>(c, t0, rows)) * c.dim + c.d0;
     const int64_t bytes = (rows * c.dim - c.d0) * (int64_t)sizeof(TIO);
-    const __amdgpu_buffer_rsrc_t rdu = make_rsrc((TIO *)o.du + elem, bytes);
+    const __amdgpu_buffer_rsrc_t rdu = make_rsrc((TU *)o.du + elem, bytes * S);
     const __amdgpu_buffer_rsrc_t rdd = make_rsrc((TIO *)o.ddelta + elem, bytes);
     const __amdgpu_buffer_rsrc_t rdz = make_rsrc(gated ? (TIO *)o.dz + elem : nullptr,
                                                  gated ? bytes : 0);
+    const int voff_du = S == 1 ? c.voff_store : (active ? c.voff * S : stream::kStoreOffsetOutOfRange);
     float *ldsB = lds;
     float *ldsC = lds + N * kLdsStride;
 #pragma unroll
@@ -543,7 +563,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
         const int64_t row = step_row(i, valid);
         fetch_row(brow, Bm, row);
         fetch_row(crow, Cm, row);
-        const float ut = (FIXED && !CONV) ? raw_f<TIO>(ch.u[i]) : us[i];
+        const float ut = FIXED ? raw_f<TU>(ch.u[i]) : us[i];
         const float xr = raw_f<TIO>(ch.x[i]) + c.bias;
         const float sp = softplus(xr);
         float dt = c.softplus ? sp : xr;
@@ -608,29 +628,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
         acc.dD = fmaf(dypre, ut, acc.dD);   // dy = 0 on padding steps
         acc.dbias += ddl;
         const int soff = step_soff<VAR>(c, i, rows);
-        int soff_du = soff;
-        float dxo = dut;
-        if constexpr (CONV) {
-            // through SiLU'(p) = s (1 + p (1 - s)), s = sigmoid(p), and the taps
-            const float sa = sigmoid(pre[i]);
-            const float gp = valid ? dut * (sa * fmaf(pre[i], 1.0f - sa, 1.0f)) : 0.0f;
-            acc.dcb += gp;
-#pragma unroll
-            for (int m = 0; m < kMaxConv; ++m)
-                acc.dcw[m] = fmaf(gp, xw[i + m], acc.dcw[m]);
-            dxo = fmaf(c.cw[kMaxConv - 1], gp, acc.ring[0]);
-#pragma unroll
-            for (int j = 0; j < kHalo - 1; ++j)
-                acc.ring[j] = fmaf(c.cw[kMaxConv - 2 - j], gp, acc.ring[j + 1]);
-            acc.ring[kHalo - 1] = c.cw[0] * gp;
-            // the last kHalo steps of a part followed by another: share to the workspace
-            const int64_t s = t0 + i;
-            if (xown && valid && s >= c.l_end - kHalo) {
-                xown[(c.l_end - 1 - s) * kLanes] = dxo;
-                soff_du = stream::kStoreOffsetOutOfRange;
-            }
-        }
-        buf_store(rdu, c.voff_store, soff_du, dxo, (TIO *)nullptr);
+        buf_store(rdu, voff_du, widen_soff<S>(soff), dut, (TU *)nullptr);
         buf_store(rdd, c.voff_store, soff, ddl, (TIO *)nullptr);
         if (gated) {
             const float dz = dyt * ypre * sz * (1.0f + zt * (1.0f - sz));
@@ -663,83 +661,67 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const BwdChunk &pr
 }
 
 template <int N, bool POW, int VAR, typename TIO>
-__device__ __forceinline__ void bwd_part(const TIO *u, const TIO *delta, const TIO *z,
-                                         const TIO *dy, const TIO *Bm, const TIO *Cm,
-                                         const WaveCtx &c, const float *ck, const float (&A2)[N],
-                                         const float (&invA)[N], float (&g)[N], float (&dA)[N],
-                                         BwdAcc &acc, const BwdOut &o, int64_t grp_in_row,
-                                         int64_t batch, float *lds, int lane, bool active,
-                                         float *xown)
+__device__ __forceinline__ void bwd_part(const UType<VAR, TIO> *u, const TIO *delta,
+                                         const TIO *z, const TIO *dy, const TIO *Bm,
+                                         const TIO *Cm, const WaveCtx &c, const float *ck,
+                                         const float (&A2)[N], const float (&invA)[N],
+                                         float (&g)[N], float (&dA)[N], BwdAcc &acc,
+                                         const BwdOut &o, int64_t grp_in_row, int64_t batch,
+                                         float *lds, int lane, bool active)
 {
-    constexpr bool CONV = (VAR & kVarConv) != 0;
     const bool gated = z != nullptr;
     const int64_t nchunks = (c.l_end - c.l_begin + TT - 1) / TT;
     int64_t t0 = c.l_begin + (nchunks - 1) * TT;
     BwdChunk A, B;
-    if constexpr (CONV) {
-        // The conv window of a chunk is in the chunk before it, so the loads
-        // run two chunks ahead (that chunk has arrived when the window is
-        // read); the chunk before the part is loaded for its window too.
-        const int64_t lo = c.l_begin >= TT ? c.l_begin - TT : 0;
-        BwdChunk C;
-        load_bwd_chunk<VAR>(A, u, delta, z, dy, c, t0, true, lo);
-        load_bwd_chunk<VAR>(B, u, delta, z, dy, c, t0 - TT, true, lo);
-        for (;;) {
-            load_bwd_chunk<VAR>(C, u, delta, z, dy, c, t0 - 2 * TT, true, lo);
-            bwd_chunk<N, POW, VAR>(A, B, Bm, Cm, c, t0, ck + (t0 / TT) * (N * kLanes), A2, invA,
-                                   g, dA, acc, gated, o, grp_in_row, batch, lds, lane, active,
-                                   xown);
-            t0 -= TT;
-            if (t0 < c.l_begin)
-                break;
-            A = B;
-            B = C;
-        }
-    } else {
-        load_bwd_chunk<VAR>(A, u, delta, z, dy, c, t0, true, c.l_begin);
-        for (;;) {
-            load_bwd_chunk<VAR>(B, u, delta, z, dy, c, t0 - TT, true, c.l_begin);
-            bwd_chunk<N, POW, VAR>(A, A, Bm, Cm, c, t0, ck + (t0 / TT) * (N * kLanes), A2, invA,
-                                   g, dA, acc, gated, o, grp_in_row, batch, lds, lane, active,
-                                   nullptr);
-            t0 -= TT;
-            if (t0 < c.l_begin)
-                break;
-            A = B;
-        }
+    load_bwd_chunk<VAR>(A, u, delta, z, dy, c, t0, true, c.l_begin);
+    for (;;) {
+        load_bwd_chunk<VAR>(B, u, delta, z, dy, c, t0 - TT, true, c.l_begin);
+        bwd_chunk<N, POW, VAR>(A, Bm, Cm, c, t0, ck + (t0 / TT) * (N * kLanes), A2, invA, g, dA,
+                               acc, gated, o, grp_in_row, batch, lds, lane, active);
+        t0 -= TT;
+        if (t0 < c.l_begin)
+            break;
+        A = B;
     }
 }
 
 // Main-pass occupancy: two waves per SIMD (256 VGPRs) up to N = 16; one
 // (512 VGPRs, spills to AGPRs) from N = 32 on, where two waves spill 474
 // VGPRs to scratch (batch 8, L 2048, D 1536, N 32: 4.35 -> 1.74 ms), and for
-// the variants from N = 16 on, whose extra per-state terms would spill at 256.
+// exact ZOH from N = 16 on, whose extra per-state terms would spill at 256.
 template <int N, int VAR>
 constexpr int bwd_waves_per_eu()
 {
     if (N > 16)
         return 1;
-    if ((VAR & (kVarZoh | kVarConv)) != 0 && N >= 16)
+    if ((VAR & kVarZoh) != 0 && N >= 16)
         return 1;
     return 2;
 }
 
 // One wave per workgroup: the LDS transposes synchronise with __syncthreads.
+// u_in: the scan input, the I/O type or (kVarUf) fp32; o.du takes its
+// gradient in the same type and layout (with kVarUf, u and o.du may be one
+// buffer: a wave reads each element of its part before it stores there).
+// u_in is untyped so that the kernel's symbol names no type computed from
+// the variant bits: such a name refers to the unnamed enum of those bits,
+// which the host and device compilations number differently, and the host
+// would then register a symbol that the device code does not define.
 template <int N, int VAR, typename TIO>
 __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<N, VAR>()))) void bwd_main_kernel(
-    const TIO *__restrict__ u, const TIO *__restrict__ delta, const TIO *__restrict__ z,
+    const void *u_in, const TIO *__restrict__ delta, const TIO *__restrict__ z,
     const TIO *__restrict__ dy, const float *__restrict__ A, const TIO *__restrict__ Bm,
     const TIO *__restrict__ Cm, const float *__restrict__ D_skip,
     const float *__restrict__ delta_bias, int delta_softplus, const float *__restrict__ dh_last,
     const float *__restrict__ aentry, const float *__restrict__ ckpt, BwdOut o, int64_t L,
-    int64_t dim, int64_t batch, int64_t groups, int parts, int64_t part_len, int64_t nck,
-    ExtParams ext)
+    int64_t dim, int64_t batch, int64_t groups, int parts, int64_t part_len, int64_t nck, int rev)
 {
     constexpr bool ZOH = (VAR & kVarZoh) != 0;
-    constexpr bool CONV = (VAR & kVarConv) != 0;
+    static_assert((VAR & kVarConv) == 0, "the main pass takes the conv prologue's output");
+    const UType<VAR, TIO> *u = (const UType<VAR, TIO> *)u_in;
     __shared__ float lds[2 * N * kLdsStride];
     WaveSetup w;
-    if (!setup_wave(w, blockIdx.x, groups, parts, L, dim, part_len, (int)sizeof(TIO), ext.rev))
+    if (!setup_wave(w, blockIdx.x, groups, parts, L, dim, part_len, (int)sizeof(TIO), rev))
         return;
     WaveCtx &c = w.c;
     c.softplus = delta_softplus;
@@ -747,8 +729,6 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     const bool pow_path = load_A<N, ZOH>(A, w.d, A2, invA, c);
     c.bias = delta_bias ? delta_bias[w.d] : 0.0f;
     c.Dd = D_skip ? D_skip[w.d] : 0.0f;
-    if constexpr (CONV)
-        stream::conv_taps(c, ext, w.d);
     // adjoint entering the part's last step from the right: dh_last folded
     // through the adjoint summaries of the later parts (aentry, null when the
     // sequence is not split)
@@ -765,33 +745,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     for (int n = 0; n < N; ++n)
         dA[n] = 0.0f;
     BwdAcc acc;
-    acc.dD = acc.dbias = acc.dcb = 0.0f;
-#pragma unroll
-    for (int m = 0; m < kMaxConv; ++m)
-        acc.dcw[m] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kHalo; ++j)
-        acc.ring[j] = 0.0f;
+    acc.dD = acc.dbias = 0.0f;
     const int64_t groups_per_row = (dim + kLanes - 1) / kLanes;
     const int64_t gir = w.grp % groups_per_row;
     const float *ck = ckpt + w.grp * nck * (N * kLanes) + w.lane;
-    const int64_t wave_slot = w.grp * parts + w.part;
-    float *xown = (CONV && w.part < parts - 1) ? o.xown + wave_slot * kHalo * kLanes + w.lane
-                                               : nullptr;
     if (pow_path)
         bwd_part<N, true, VAR>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir, batch,
-                               lds, w.lane, w.active, xown);
+                               lds, w.lane, w.active);
     else
         bwd_part<N, false, VAR>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir,
-                                batch, lds, w.lane, w.active, xown);
-    if constexpr (CONV) {
-        if (w.part > 0) {
-            float *xc = o.xcarry + wave_slot * kHalo * kLanes + w.lane;
-#pragma unroll
-            for (int j = 0; j < kHalo; ++j)
-                xc[j * kLanes] = acc.ring[j];
-        }
-    }
+                                batch, lds, w.lane, w.active);
     if (w.active) {
         const int64_t slot = c.b * parts + w.part;
 #pragma unroll
@@ -799,15 +762,6 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
             o.pA[(slot * dim + w.d) * N + n] = dA[n];
         o.pD[slot * dim + w.d] = acc.dD;
         o.pbias[slot * dim + w.d] = acc.dbias;
-        if constexpr (CONV) {
-            // tap m of the zero-padded window is conv_weight[d, m - (4 - conv_k)]
-            const int k = ext.conv_k;
-#pragma unroll
-            for (int m = 0; m < kMaxConv; ++m)
-                if (m >= kMaxConv - k)
-                    o.pW[(slot * dim + w.d) * k + m - (kMaxConv - k)] = acc.dcw[m];
-            o.pWb[slot * dim + w.d] = acc.dcb;
-        }
         if (w.part == 0 && o.dh0) {
 #pragma unroll
             for (int n = 0; n < N; ++n)
@@ -816,26 +770,127 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     }
 }
 
-// Conv prologue: dx of the last kHalo steps of every part but the last, the
-// part's own share plus the next part's.
+// Conv prologue epilogue: from gu (the main pass's fp32 gradient of the scan
+// input) and the raw input x, gp_s = gu_s SiLU'(p_s), dx, and per-part sums
+// of dconv_w, dconv_b.  One wave per (channel group, part), walking scan
+// steps l_begin .. l_end + kHalo - 1 in batches of TTE (the next batch's
+// loads in flight while one computes): p_s from x_{s-3..s} (a register
+// window, filled first with the kHalo steps before the part), then
+// dx_{s-3} = sum_m w_m gp_{s-m} once gp_s is known.  Steps past the part
+// recompute the next part's first gp values; steps past L read zeros
+// (gp = 0).
+constexpr int TTE = 8;
+
 template <typename TIO>
-__global__ __launch_bounds__(kLanes * 4) void bwd_conv_fixup_kernel(
-    TIO *__restrict__ du, const float *__restrict__ xown, const float *__restrict__ xcarry,
-    int64_t L, int64_t dim, int64_t groups, int parts, int64_t part_len, int rev)
+__global__ __launch_bounds__(kLanes * 4) void bwd_conv_epilogue_kernel(
+    const TIO *__restrict__ x, const float *__restrict__ gu, TIO *__restrict__ dx,
+    float *__restrict__ pW, float *__restrict__ pWb, ExtParams ext, int64_t L, int64_t dim,
+    int64_t groups, int parts, int64_t part_len)
 {
+    constexpr int S = (int)(sizeof(float) / sizeof(TIO));
     WaveSetup w;
     const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (!setup_wave(w, gw, groups, parts - 1, L, dim, part_len, (int)sizeof(TIO), rev))
+    if (!setup_wave(w, gw, groups, parts, L, dim, part_len, (int)sizeof(TIO), ext.rev))
         return;
-    const WaveCtx &c = w.c;
-    const int64_t slot = w.grp * parts + w.part;
+    WaveCtx &c = w.c;
+    stream::conv_taps(c, ext, w.d);
+    float xw[kHalo], gw3[kHalo];   // x and gp of the kHalo steps before s, oldest first
+    stream::conv_window<kVarExt>(xw, c, x, w.d);
 #pragma unroll
-    for (int j = 0; j < kHalo; ++j) {
-        const float v = xown[(slot * kHalo + j) * kLanes + w.lane] +
-                        xcarry[((slot + 1) * kHalo + j) * kLanes + w.lane];
-        const int64_t s = c.l_end - 1 - j;
-        if (w.active)
-            store_elem(du, scan_row<kVarExt>(c, s) * dim + w.d, v);
+    for (int j = 0; j < kHalo; ++j)
+        gw3[j] = 0.0f;
+    float dw[kMaxConv], db = 0.0f;
+#pragma unroll
+    for (int m = 0; m < kMaxConv; ++m)
+        dw[m] = 0.0f;
+    const int64_t lo = c.l_begin, own_end = c.l_end;
+    const int64_t hi = own_end + kHalo < L ? own_end + kHalo : L;   // steps read
+    // dx of a finished step: its share of gp from steps s-3..s
+    auto emit = [&](int64_t s, float gp) {
+        const int64_t sd = s - kHalo;
+        if (sd >= lo) {
+            float v = c.cw[0] * gp;
+#pragma unroll
+            for (int j = 0; j < kHalo; ++j)
+                v = fmaf(c.cw[kHalo - j], gw3[j], v);
+            if (w.active)
+                store_elem(dx, scan_row<kVarExt>(c, sd) * dim + w.d, v);
+        }
+#pragma unroll
+        for (int j = 0; j < kHalo - 1; ++j)
+            gw3[j] = gw3[j + 1];
+        gw3[kHalo - 1] = gp;
+    };
+    auto load = [&](uint32_t (&xr)[TTE], uint32_t (&gr)[TTE], int64_t s0) {
+        int64_t rows = hi - s0;
+        rows = rows < 0 ? 0 : (rows > TTE ? TTE : rows);
+        const int64_t elem = rows > 0 ? (c.bL + run_t_lo<kVarExt>(c, s0, rows)) * dim + c.d0 : 0;
+        const int64_t bytes = rows > 0 ? (rows * dim - c.d0) * (int64_t)sizeof(TIO) : 0;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + elem, bytes);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu + elem, bytes * S);
+#pragma unroll
+        for (int i = 0; i < TTE; ++i) {
+            const int soff = step_soff<kVarExt>(c, i, (int)rows);
+            xr[i] = buf_load_raw(rx, c.voff, soff, x);
+            gr[i] = buf_load_raw(rg, c.voff * S, widen_soff<S>(soff), gu);
+        }
+    };
+    auto run = [&](const uint32_t (&xr)[TTE], const uint32_t (&gr)[TTE], int64_t s0) {
+#pragma unroll
+        for (int i = 0; i < TTE; ++i) {
+            const int64_t s = s0 + i;
+            if (s >= hi)
+                break;   // uniform
+            const float xs = raw_f<TIO>(xr[i]);
+            float p = c.cb;
+#pragma unroll
+            for (int j = 0; j < kHalo; ++j)
+                p = fmaf(c.cw[j], xw[j], p);
+            p = fmaf(c.cw[kHalo], xs, p);
+            // SiLU'(p) = s (1 + p (1 - s)), s = sigmoid(p)
+            const float sa = sigmoid(p);
+            const float gp = __uint_as_float(gr[i]) * (sa * fmaf(p, 1.0f - sa, 1.0f));
+            if (s < own_end) {   // uniform
+                db += gp;
+#pragma unroll
+                for (int j = 0; j < kHalo; ++j)
+                    dw[j] = fmaf(gp, xw[j], dw[j]);
+                dw[kHalo] = fmaf(gp, xs, dw[kHalo]);
+            }
+            emit(s, gp);
+#pragma unroll
+            for (int j = 0; j < kHalo - 1; ++j)
+                xw[j] = xw[j + 1];
+            xw[kHalo - 1] = xs;
+        }
+    };
+    uint32_t xa[TTE], ga[TTE], xb[TTE], gb[TTE];
+    int64_t s0 = lo;
+    load(xa, ga, s0);
+    for (;;) {
+        load(xb, gb, s0 + TTE);
+        run(xa, ga, s0);
+        s0 += TTE;
+        if (s0 >= hi)
+            break;
+        load(xa, ga, s0 + TTE);
+        run(xb, gb, s0);
+        s0 += TTE;
+        if (s0 >= hi)
+            break;
+    }
+    // at the sequence end: the steps past L have gp = 0
+    for (int64_t s = hi; s < own_end + kHalo; ++s)
+        emit(s, 0.0f);
+    if (w.active) {
+        const int64_t slot = c.b * parts + w.part;
+        // tap m of the zero-padded window is conv_weight[d, m - (4 - conv_k)]
+        const int k = ext.conv_k;
+#pragma unroll
+        for (int m = 0; m < kMaxConv; ++m)
+            if (m >= kMaxConv - k)
+                pW[(slot * dim + w.d) * k + m - (kMaxConv - k)] = dw[m];
+        pWb[slot * dim + w.d] = db;
     }
 }
 
@@ -861,8 +916,8 @@ hipError_t launch_colsums(const ColsumJobs &jobs, hipStream_t s);
 struct BwdLayout {
     StreamPlan p;
     int64_t nck, gpr;
-    size_t fsumm, asumm, fentry, aentry, carry, ckpt, pB, pC, pA, pD, pbias, pW, pWb, xown,
-        xcarry, total;   // byte offsets
+    size_t fsumm, asumm, fentry, aentry, carry, ckpt, pB, pC, pA, pD, pbias, pW, pWb, uconv,
+        total;   // byte offsets
 };
 BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N);
 
@@ -875,14 +930,17 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     float *fsumm = (float *)(base + w.fsumm), *asumm = (float *)(base + w.asumm);
     float *fentry = (float *)(base + w.fentry), *aentry = (float *)(base + w.aentry);
     float *ckpt = (float *)(base + w.ckpt);
+    // conv prologue: the scan inputs (fp32, written by the checkpoint pass),
+    // then in place their gradient (the main pass), read by the epilogue
+    float *uconv = (float *)(base + w.uconv);
+    float *pW = (float *)(base + w.pW), *pWb = (float *)(base + w.pWb);
     BwdOut o;
-    o.du = a.du; o.ddelta = a.ddelta; o.dz = a.dz;
+    o.du = CONV ? (void *)uconv : a.du;
+    o.ddelta = a.ddelta; o.dz = a.dz;
     o.pB = (float *)(base + w.pB); o.pC = (float *)(base + w.pC);
     o.pA = (float *)(base + w.pA); o.pD = (float *)(base + w.pD);
     o.pbias = (float *)(base + w.pbias);
     o.dh0 = a.dh0;
-    o.pW = (float *)(base + w.pW); o.pWb = (float *)(base + w.pWb);
-    o.xown = (float *)(base + w.xown); o.xcarry = (float *)(base + w.xcarry);
     ExtParams x;
     x.conv_w = CONV ? e.conv_w : nullptr;
     x.conv_b = CONV ? e.conv_b : nullptr;
@@ -912,8 +970,9 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
                            (const TIO *)a.fwd.u, (const TIO *)a.fwd.delta, (const TIO *)a.fwd.z,
                            (const TIO *)a.dy, a.fwd.A, (const TIO *)a.fwd.Bm,
                            (const TIO *)a.fwd.Cm, a.fwd.delta_bias, a.fwd.delta_softplus,
-                           a.fwd.h0, (const float *)(split ? fentry : nullptr), asumm, ckpt, w.nck,
-                           x, a.fwd.L, a.fwd.dim, p.groups, p.parts, p.part_len, nadj, nck);
+                           a.fwd.h0, (const float *)(split ? fentry : nullptr), asumm, ckpt,
+                           uconv, w.nck, x, a.fwd.L, a.fwd.dim, p.groups, p.parts, p.part_len,
+                           nadj, nck);
     };
     // entry states of the parts: from the left (h0) and from the right (dh_last)
     auto carry_fwd = [&]() {
@@ -946,20 +1005,32 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
             return err;
     }
     const int64_t waves = p.groups * p.parts;
-    hipLaunchKernelGGL((bwd_main_kernel<N, VAR, TIO>), dim3((unsigned)waves), dim3(kLanes), 0, s,
-                       (const TIO *)a.fwd.u, (const TIO *)a.fwd.delta, (const TIO *)a.fwd.z,
-                       (const TIO *)a.dy, a.fwd.A, (const TIO *)a.fwd.Bm, (const TIO *)a.fwd.Cm,
-                       a.fwd.D_skip, a.fwd.delta_bias, a.fwd.delta_softplus, a.dh_last,
-                       (const float *)(split ? aentry : nullptr), ckpt, o, a.fwd.L, a.fwd.dim,
-                       a.fwd.batch, p.groups, p.parts, p.part_len, w.nck, x);
-    if ((err = hipGetLastError()) != hipSuccess)
+    auto main_pass = [&](auto kernel, auto u) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)waves), dim3(kLanes), 0, s, u,
+                           (const TIO *)a.fwd.delta, (const TIO *)a.fwd.z, (const TIO *)a.dy,
+                           a.fwd.A, (const TIO *)a.fwd.Bm, (const TIO *)a.fwd.Cm, a.fwd.D_skip,
+                           a.fwd.delta_bias, a.fwd.delta_softplus, a.dh_last,
+                           (const float *)(split ? aentry : nullptr), ckpt, o, a.fwd.L,
+                           a.fwd.dim, a.fwd.batch, p.groups, p.parts, p.part_len, w.nck, x.rev);
+        return hipGetLastError();
+    };
+    if constexpr (!CONV) {
+        err = main_pass(bwd_main_kernel<N, VAR, TIO>, (const TIO *)a.fwd.u);
+    } else if constexpr ((VAR & kVarZoh) != 0) {
+        err = main_pass(bwd_main_kernel<N, (VAR & ~kVarConv) | kVarUf, TIO>, (const float *)uconv);
+    } else {
+        // Euler B_bar: the plain pass on fp32 inputs, direction fixed at
+        // compile time
+        err = x.rev ? main_pass(bwd_main_kernel<N, kVarRev | kVarUf, TIO>, (const float *)uconv)
+                    : main_pass(bwd_main_kernel<N, kVarUf, TIO>, (const float *)uconv);
+    }
+    if (err != hipSuccess)
         return err;
-    if (CONV && p.parts > 1) {
-        const int64_t fw = p.groups * (p.parts - 1);
-        hipLaunchKernelGGL((bwd_conv_fixup_kernel<TIO>), dim3((unsigned)((fw + 3) / 4)),
-                           dim3(kLanes * 4), 0, s, (TIO *)a.du, (const float *)o.xown,
-                           (const float *)o.xcarry, a.fwd.L, a.fwd.dim, p.groups, p.parts,
-                           p.part_len, x.rev);
+    if constexpr (CONV) {
+        hipLaunchKernelGGL((bwd_conv_epilogue_kernel<TIO>), dim3((unsigned)((waves + 3) / 4)),
+                           dim3(kLanes * 4), 0, s, (const TIO *)a.fwd.u, (const float *)uconv,
+                           (TIO *)a.du, pW, pWb, x, a.fwd.L, a.fwd.dim, p.groups, p.parts,
+                           p.part_len);
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }
@@ -972,8 +1043,8 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     jobs.add(o.pD, a.dD, a.fwd.dim, slots);
     jobs.add(o.pbias, a.ddelta_bias, a.fwd.dim, slots);
     if (CONV) {
-        jobs.add(o.pW, a.dconv_w, a.fwd.dim * x.conv_k, slots);
-        jobs.add(o.pWb, a.dconv_b, a.fwd.dim, slots);
+        jobs.add(pW, a.dconv_w, a.fwd.dim * x.conv_k, slots);
+        jobs.add(pWb, a.dconv_b, a.fwd.dim, slots);
     }
     return launch_colsums(jobs, s);
 }

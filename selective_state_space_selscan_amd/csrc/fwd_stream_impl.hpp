@@ -70,8 +70,9 @@ static_assert(TT <= kStreamTT, "plan rounds parts to kStreamTT steps");
 
 // kVarRev: reverse direction fixed at compile time, used alone (no kVarExt):
 // the reverse-only call then compiles to the default's code with the
-// addressing mirrored.
-enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4, kVarRev = 8 };
+// addressing mirrored.  kVarUf (backward only): the scan input is fp32 bits
+// whatever the I/O type (the conv prologue's output, computed beforehand).
+enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4, kVarRev = 8, kVarUf = 16 };
 constexpr int kMaxConv = 4;
 
 // Variant arguments of the kernel (ignored when VAR = 0).
@@ -215,7 +216,7 @@ template <int VAR, typename TIO>
 __device__ __forceinline__ float step_input(uint32_t raw, const WaveCtx &c,
                                             float (&win)[kMaxConv - 1])
 {
-    const float x = raw_to_f32(raw, tag<TIO>());
+    const float x = (VAR & kVarUf) != 0 ? __uint_as_float(raw) : raw_to_f32(raw, tag<TIO>());
     if constexpr ((VAR & kVarConv) != 0) {
         float acc = c.cb;
 #pragma unroll

@@ -51,6 +51,20 @@ def test_library_exports_every_declared_symbol():
     assert L.selscan_abi_version() == header_constant("SELSCAN_ABI_VERSION")
 
 
+def test_every_registered_kernel_name_has_device_code():
+    """The host side of the library launches a kernel by its mangled name,
+    which must name a kernel descriptor (``<name>.kd``) in the device code.
+    A name that mentions an unnamed type (``$_<n>``, numbered per compilation
+    pass) can differ between the two and the launch then aborts."""
+    blob = open(ss._abi._LIB_PATH, "rb").read()
+    names = set(m.decode() for m in re.findall(rb"_ZN7selscan[A-Za-z0-9_$.]*", blob))
+    descriptors = {n[:-3] for n in names if n.endswith(".kd")}
+    kernels = {n for n in names if "." not in n and "kernel" in n and "__device_stub__" not in n}
+    assert descriptors, "no device code found in the library"
+    assert not [n for n in names if "$_" in n]
+    assert kernels <= descriptors, sorted(kernels - descriptors)[:3]
+
+
 def test_status_strings_and_supported_n():
     L = ss.lib()
     for s in range(10):
