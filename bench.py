@@ -69,7 +69,7 @@ def algorithmic_bytes(batch, L, dim, N, es, gate, with_last=False, with_h0=False
     return b
 
 
-def algorithmic_valu_slots(N, gate, es, general_a=False):
+def algorithmic_valu_slots(N, gate, es, general_a=False, flags=0, conv_k=0):
     """fp32 VALU issue slots one (b, l, d) element needs on gfx950 without
     packed instructions.  A transcendental (exp2, log2, rcp) takes two slots.
     For A of the S4D-real form (A[d,n] = (n+1) A[d,0], every workload here):
@@ -81,13 +81,26 @@ def algorithmic_valu_slots(N, gate, es, general_a=False):
       gate:        widen z (1 if bf16), SiLU (exp, rcp: 4 slots, + 2), y*g (1)
     For a general A (general_a), A_bar = exp2(Delta A[d,n] log2 e) per state:
     a multiply and an exp2 (3 slots) in place of the power chain's multiply,
-    and no r: 6 N + the per-element work less 3."""
+    and no r: 6 N + the per-element work less 3.
+    Variants (``flags``, ``conv_k`` as for selscan_fwd_ex; the power chain):
+      reverse:   addressing only                                    -> + 0
+      exact ZOH: B_bar_n = c_n B_n with c_n = em S_n / (n+1), S_n the running
+                 sum of the powers: per state the sum, S_n B_n and the scale
+                 (3); per element em = (r - 1) / A[d,0] with its series
+                 branch (9) in place of Delta*u (1)                -> + 3 N + 8
+      conv:      k taps of the causal conv (k FMAs) and SiLU (exp, rcp: 4
+                 slots, + 2) of the scan input                     -> + k + 6"""
     bf = 1 if es == 2 else 0
     per = 4 * N + 2 * bf + 1 + 6 + 1 + 3 + 1 + bf
     if gate:
         per += bf + 6 + 1
     if general_a:
+        assert not flags & VARIANT_FLAGS["zoh"], "general A with exact ZOH is not counted"
         per += 2 * N - 3
+    if flags & VARIANT_FLAGS["zoh"]:
+        per += 3 * N + 8
+    if conv_k:
+        per += conv_k + 6
     return per
 
 
@@ -235,7 +248,7 @@ def decode_bytes(batch, dim, N, es, gate):
             + 2 * batch * N * es + dim * N * 4 + 2 * dim * 4)
 
 
-def bench_decode(w, steps, warmup):
+def bench_decode(w, steps, warmup, ramp_ms=0.0):
     """Decode: ``steps`` single-token selscan_state_update calls on the resident
     fp32 state (batch, dim, N).  Warm: back-to-back steps, the 84 MB state may
     stay in the 256 MB last-level cache.  Cold: a 1 GiB buffer is read before
@@ -259,6 +272,7 @@ def bench_decode(w, steps, warmup):
         ss.selscan_state_update(state, t["u"], t["delta"], A, t["Bm"], t["Cm"], D, t["z"], bias,
                                 True, y=ys[i % len(ins)], stream=stream)
 
+    ramp = clock_ramp(step, ramp_ms)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -294,6 +308,7 @@ def bench_decode(w, steps, warmup):
         "data": "synthetic (seeded per step)",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "N": w.N,
                    "state": "fp32 resident"},
+        "clock_ramp": {"calls": ramp[0], "ms": ramp[1]},
         "step_ms_warm": warm_ms, "step_ms_cold": cold_ms,
         "device_copy_gbps": device_copy_gbps(dev),
         "roofline": {"bound": "hbm", "achieved": nb / (cold_ms * 1e-3) / 1e9,
@@ -306,8 +321,31 @@ def bench_decode(w, steps, warmup):
     print(json.dumps(res), flush=True)
 
 
-def timed_steps(step, steps, warmup, stream, percall=50):
-    """``warmup`` untimed steps, then exactly ``steps`` steps back to back,
+def clock_ramp(step, ramp_ms):
+    """Untimed steps for at least ``ramp_ms`` of wall time before the warmup
+    steps.  An idle GPU runs its first milliseconds of work at lower clocks
+    (the 130M-layer forward with 5 warmup calls: 139 us per call over the
+    next 20, rising from 134 to 145; after 250 ms of calls 122 us, falling
+    to 119), so a short warmup alone would time the ramp rather than the
+    kernels.  Returns (calls, ms)."""
+    import torch
+
+    if ramp_ms <= 0:
+        return 0, 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    calls = 0
+    while (time.perf_counter() - t0) * 1e3 < ramp_ms:
+        for _ in range(64):
+            step(calls)
+            calls += 1
+        torch.cuda.synchronize()
+    return calls, (time.perf_counter() - t0) * 1e3
+
+
+def timed_steps(step, steps, warmup, stream, percall=50, ramp_ms=0.0):
+    """A clock ramp of ``ramp_ms`` (clock_ramp), ``warmup`` untimed steps,
+    then exactly ``steps`` steps back to back,
     bracketed by a synchronize on both sides (host clock) and by HIP events on
     the launch stream (device clock): the average call duration is the
     interval from the first event to the last / ``steps``.  Events also mark
@@ -316,9 +354,11 @@ def timed_steps(step, steps, warmup, stream, percall=50):
     ``percall`` further steps, each between its own pair of events, for the
     spread of single calls; they are not part of the timed region (an event
     pair per call adds a small bubble of its own).  Returns (wall s, mean
-    call ms, per-call ms array, mean call ms per quarter)."""
+    call ms, per-call ms array, mean call ms per quarter, (ramp calls, ramp
+    ms))."""
     import torch
 
+    ramp = clock_ramp(step, ramp_ms)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -341,7 +381,7 @@ def timed_steps(step, steps, warmup, stream, percall=50):
         step(warmup + steps + i)
         y.record(stream)
     torch.cuda.synchronize()
-    return wall, call_mean, np.array([x.elapsed_time(y) for x, y in ev]), quarters
+    return wall, call_mean, np.array([x.elapsed_time(y) for x, y in ev]), quarters, ramp
 
 
 def device_copy_gbps(dev, nbytes=1 << 29, reps=10):
@@ -381,10 +421,11 @@ def bwd_valu_slots(N, gate, es, flags=0, conv_k=0):
         dDelta and dA); the LDS sums 2                            -> 56 N
     Per element about 60 (softplus and sigmoid twice, SiLU and its derivative,
     widening, the per-element gradients and stores); the conv prologue adds
-    48 (the conv and SiLU of the scan input recomputed in the main, summary
-    and checkpoint passes, 10 each, and in the main pass the conv's own
-    backward: SiLU' of the pre-activation, the dconv_w and dconv_b sums and
-    the transposed conv of dx, 18)."""
+    48: the conv and SiLU of the scan input in the summary and checkpoint
+    passes (10 each; the main pass reads the checkpoint pass's fp32 output),
+    and the epilogue's conv backward (28: the pre-activation again, its
+    sigmoid, SiLU', the dconv_w and dconv_b sums and the transposed conv of
+    dx)."""
     per_n = 56 if flags & VARIANT_FLAGS["zoh"] else 16
     return per_n * N + 60 + (48 if conv_k else 0)
 
@@ -437,7 +478,8 @@ def bench_bwd(w, args):
         ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"], t["z"],
                        t["delta_bias"], True, None, None, workspace=ws, stream=stream)
 
-    wall, call_mean, call_ms, quarters = timed_steps(step, args.steps, args.warmup, stream)
+    wall, call_mean, call_ms, quarters, ramp = timed_steps(step, args.steps, args.warmup, stream,
+                                                             ramp_ms=args.ramp_ms)
     es = 2 if w.dtype == si.BF16 else 4
     elems = w.batch * w.L * w.dim
     slots_el = bwd_valu_slots(w.N, w.gate, es, vflags, vconv) + (
@@ -459,6 +501,7 @@ def bench_bwd(w, args):
         "config": {"workload": w.name, "pass": args.which, "batch": w.batch, "L": w.L,
                    "dim": w.dim,
                    "N": w.N, "gate": w.gate},
+        "clock_ramp": {"calls": ramp[0], "ms": ramp[1]},
         "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms)),
                     "timed_quarters": quarters},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_SLOTS / 1e9,
@@ -547,9 +590,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed steps first: about 0.1 s of work, so that the clocks have "
-                         "ramped up before the timed region")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before the timed ones")
+    ap.add_argument("--ramp-ms", type=float, default=500.0,
+                    help="untimed steps for this long (wall clock) before the warmup steps, so "
+                         "that the clocks have ramped up (0: none); reported as clock_ramp")
     ap.add_argument("--workload", default="mamba130m_layer")
     ap.add_argument("--rotate", type=int, default=4, help="input-set copies to rotate")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -575,7 +619,7 @@ def main():
               "so throughput on several GPUs is not measured.", file=sys.stderr)
         sys.exit(2)
     if w.decode_steps:
-        bench_decode(w, args.steps, args.warmup)
+        bench_decode(w, args.steps, args.warmup, args.ramp_ms)
         return
     if args.pmc_run:
         pmc_run(w)
@@ -628,12 +672,13 @@ def main():
                        y=ys[i % args.rotate], h_last=hls[i % args.rotate],
                        workspace=wss[i % args.rotate], stream=stream)
 
-    wall, call_mean, call_ms, quarters = timed_steps(step, args.steps, args.warmup, stream)
+    wall, call_mean, call_ms, quarters, ramp = timed_steps(step, args.steps, args.warmup, stream,
+                                                             ramp_ms=args.ramp_ms)
 
     elems = w.batch * w.L * w.dim
     ms_per_step = 1e3 * wall / args.steps
     abytes = algorithmic_bytes(w.batch, w.L, w.dim, w.N, es, w.gate, w.want_last_state)
-    slots_el = algorithmic_valu_slots(w.N, w.gate, es, general_a)
+    slots_el = algorithmic_valu_slots(w.N, w.gate, es, general_a, vflags, vconv)
     slots = slots_el * elems
     achieved = slots / (call_mean * 1e-3) / 1e9
     peak = VALU_PEAK_SLOTS / 1e9
@@ -659,6 +704,7 @@ def main():
         **({"variant": args.variant} if args.variant else {}),
         "hbm_gbps": abytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac": abytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "clock_ramp": {"calls": ramp[0], "ms": ramp[1]},
         "call_ms": {"mean": call_mean, "timed_quarters": quarters,
                     "single_call": {"p10": float(np.percentile(call_ms, 10)),
                                     "p50": float(np.median(call_ms)),

@@ -33,6 +33,13 @@ def test_valu_slot_counts():
     # general A: an exp2 (3 slots) per state for the power chain's multiply,
     # and no exp of Delta A[d,0]: 6 N + 20
     assert bench.algorithmic_valu_slots(16, True, 2, general_a=True) == 116
+    # forward variants: reverse is addressing only; exact ZOH 3 N + 8 more
+    # (the running power sum, its product with B, the scale; the coefficient
+    # em per element), the conv prologue k taps and SiLU (k + 6)
+    assert bench.algorithmic_valu_slots(16, True, 2, flags=2) == 87
+    assert bench.algorithmic_valu_slots(16, True, 2, flags=1) == 87 + 48 + 8
+    assert bench.algorithmic_valu_slots(16, True, 2, conv_k=4) == 87 + 10
+    assert bench.algorithmic_valu_slots(16, True, 2, flags=3, conv_k=4) == 87 + 56 + 10
     # backward, counted per variant: 16 N + 60 (Euler), 56 N + 60 (exact ZOH),
     # and 48 more per element with the conv prologue
     assert bench.bwd_valu_slots(16, True, 2) == 316
