@@ -61,8 +61,12 @@ __device__ __forceinline__ const T *tag()
     return (const T *)nullptr;
 }
 
-// Raw (not yet widened) element loads: the 16-bit pattern of a bf16 value or
-// the 32 bits of an fp32 value, widened with raw_to_f32 at the point of use.
+// Element loads that keep the fp32 bit pattern in a uint32_t (held in the
+// prefetch buffers, turned into a float with raw_to_f32 at the point of use):
+// an fp32 value as loaded; a bf16 value shifted into the top half (its fp32
+// pattern) right at the load.  Shifting there, where the compiler sees the
+// 16-bit load's zero extension, takes one instruction; shifting at the use,
+// across the prefetch loop, took a mask and a shift per element.
 __device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                                  const float *)
 {
@@ -71,13 +75,10 @@ __device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, int v
 __device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                                  const uint16_t *)
 {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0) << 16;
 }
 __device__ __forceinline__ float raw_to_f32(uint32_t v, const float *) { return __uint_as_float(v); }
-__device__ __forceinline__ float raw_to_f32(uint32_t v, const uint16_t *)
-{
-    return __uint_as_float(v << 16);
-}
+__device__ __forceinline__ float raw_to_f32(uint32_t v, const uint16_t *) { return __uint_as_float(v); }
 
 // One row of N values (N even) shared by the whole wave, as scalar loads.
 template <int N>
