@@ -172,6 +172,14 @@ size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_
  * y non-NULL; batch * ceil(dim/64) * max(ceil(L/16), N) < 2^31 (every launch
  * grid fits; far beyond any shape whose arrays fit in device memory).  The
  * workspace-size functions return 0 for shapes that violate these.
+ *
+ * Plans: the default is the two-pass streaming scan.  The environment
+ * variable SELSCAN_FORCE_PLAN selects an ablation with the same results
+ * within the tolerances: lookback (single pass with decoupled look-back),
+ * chunked (segments of a chunk joined through LDS) or dpp (the lanes of a
+ * wave hold 64 steps of one channel, scanned with DPP; one wave per channel,
+ * so batch * dim * parts / 4 must stay below 2^31 workgroups, else
+ * SELSCAN_ERR_HIP).  The workspace size covers every plan.
  */
 int selscan_fwd(const void *u, const void *delta, const float *A,
                 const void *Bm, const void *Cm, const float *D_skip,

@@ -48,6 +48,11 @@ struct StepArgs {
 size_t fwd_chunked_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 hipError_t launch_fwd_chunked(const FwdArgs &a, hipStream_t stream);
 
+// Forward with an in-wave DPP scan over time (ablation: lanes are the 64
+// steps of a tile of one channel): workspace bytes it needs, and the launch.
+size_t fwd_dpp_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
+hipError_t launch_fwd_dpp(const FwdArgs &a, hipStream_t stream);
+
 // Streaming forward (default): independent waves over sequence parts, with a
 // summary pre-pass when the sequence is split.
 constexpr int kStreamTT = 4;   // part lengths are multiples of this many steps

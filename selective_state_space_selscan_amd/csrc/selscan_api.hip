@@ -42,9 +42,9 @@ bool grids_fit(int64_t batch, int64_t L, int64_t dim, int64_t N)
 
 // Forward plans.  Default: the two-pass streaming kernel.  SELSCAN_FORCE_PLAN
 // = lookback selects the single-pass streaming kernel with decoupled
-// look-back; = chunked the workgroup-chunked kernel (ablations; both compute
-// the same recurrence).
-enum Plan { PLAN_STREAM, PLAN_LOOKBACK, PLAN_CHUNKED };
+// look-back; = chunked the workgroup-chunked kernel; = dpp the in-wave DPP
+// scan over time (ablations; all compute the same recurrence).
+enum Plan { PLAN_STREAM, PLAN_LOOKBACK, PLAN_CHUNKED, PLAN_DPP };
 
 // Polls before a look-back wait gives up: SELSCAN_LOOKBACK_SPIN_LIMIT (a
 // count >= 0), else the kernel's default (-1).
@@ -65,6 +65,8 @@ Plan forced_plan()
         return PLAN_CHUNKED;
     if (e && strcmp(e, "lookback") == 0)
         return PLAN_LOOKBACK;
+    if (e && strcmp(e, "dpp") == 0)
+        return PLAN_DPP;
     return PLAN_STREAM;
 }
 
@@ -216,6 +218,8 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
     switch (forced_plan()) {
     case PLAN_CHUNKED:
         return finish_launch(selscan::launch_fwd_chunked(a, (hipStream_t)stream));
+    case PLAN_DPP:
+        return finish_launch(selscan::launch_fwd_dpp(a, (hipStream_t)stream));
     case PLAN_LOOKBACK:
         return finish_launch(
             selscan::launch_fwd_lookback(a, lookback_spin_limit(), (hipStream_t)stream));
@@ -352,8 +356,10 @@ size_t selscan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_
     const size_t a = selscan::fwd_chunked_workspace_bytes(batch, L, dim, N);
     const size_t b = selscan::fwd_stream_workspace_bytes(batch, L, dim, N);
     const size_t c = selscan::fwd_lookback_workspace_bytes(batch, L, dim, N);
+    const size_t d = selscan::fwd_dpp_workspace_bytes(batch, L, dim, N);
     const size_t ab = a > b ? a : b;
-    return ab > c ? ab : c;
+    const size_t cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
 }
 
 int selscan_fwd(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,

@@ -290,7 +290,7 @@ def test_bwd_ex_rejects_invalid_arguments(name, kw, status):
 
 
 @no_gpu_only
-@pytest.mark.parametrize("plan", ["lookback", "chunked"])
+@pytest.mark.parametrize("plan", ["lookback", "chunked", "dpp"])
 def test_bwd_ex_refuses_reuse_under_forced_plan(monkeypatch, plan):
     """A forward under another plan leaves another workspace layout, so the
     backward cannot read its part state from it."""
@@ -306,7 +306,7 @@ def test_fwd_status_without_lookback_plan_touches_nothing(monkeypatch):
     plan the status call returns OK without reading the workspace (a fake
     address here) or touching the stream."""
     L = ss.lib()
-    for plan in (None, "chunked"):
+    for plan in (None, "chunked", "dpp"):
         if plan is None:
             monkeypatch.delenv("SELSCAN_FORCE_PLAN", raising=False)
         else:

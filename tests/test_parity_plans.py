@@ -1,14 +1,21 @@
-"""GPU parity of the chunked ablation plan of the forward against the fp64 oracle.
+"""GPU parity of the ablation plans of the forward against the fp64 oracle.
 
 SELSCAN_FORCE_PLAN=chunked selects the workgroup-chunked kernel: the waves of
 a workgroup share 64 channels, each runs one segment of a chunk from zero, the
 segment aggregates are exchanged through LDS with one barrier and every wave
 re-runs its segment from its true entry state (the chunked scan of the paper
-walkthrough (m.lqnn.cn) §3.2, the carry between segments staged in LDS).  It
-ships in the library and is reachable through selscan_fwd, so it faces the
-default plan's parity cases: the tiny
-and layer workloads, ragged shapes (tails, lanes past dim, many parts), every
-N in fp32 and bf16, h0, general A and softplus off.
+walkthrough (m.lqnn.cn) §3.2, the carry between segments staged in LDS).
+SELSCAN_FORCE_PLAN=dpp selects the in-wave scan over time: the lanes of a wave
+hold 64 consecutive steps of one channel and the pairs (A_bar, B_bar u) are
+scanned across them with DPP row shifts and row broadcasts (the parallel scan
+of the Mamba tutorial (pwwt.cn) §3.2 with the associative operator of the
+selection-mechanism article (discosf.com) §3.1), the state between tiles
+carried in scalar registers; shapes with few channels also split the
+sequence into parts joined by the summary and carry passes.  Both ship in
+the library and are reachable through selscan_fwd, so they face the default
+plan's parity cases: the tiny and layer workloads, ragged shapes (tails,
+lanes past dim, partial tiles, many parts), every N in fp32 and bf16, h0,
+general A and softplus off.
 """
 import numpy as np
 import pytest
@@ -21,7 +28,7 @@ from parity_util import TOL, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
-PLANS = ["chunked"]
+PLANS = ["chunked", "dpp"]
 
 
 def say(*a):
