@@ -226,7 +226,11 @@ def test_state_update_matches_forward(device, dtype):
 
 
 def test_state_update_ragged_and_small_n(device):
-    for batch, dim, N in [(1, 1, 4), (3, 100, 8), (2, 257, 32), (1, 64, 64)]:
+    """Workgroups cover a run of channels of two batch rows: odd batch
+    counts leave the second row of the last pair empty, and dims that are
+    not a multiple of the run leave lanes past dim."""
+    for batch, dim, N in [(1, 1, 4), (3, 100, 8), (2, 257, 32), (1, 64, 64), (5, 130, 16),
+                          (7, 33, 4)]:
         rng = np.random.default_rng(batch * 1000 + dim + N)
         f = lambda *s: rng.standard_normal(s).astype(np.float32)
         st = f(batch, dim, N)
@@ -242,6 +246,25 @@ def test_state_update_ragged_and_small_n(device):
         torch.cuda.synchronize()
         assert rel_err(to_np(y), ey) <= TOL["f32"]
         assert rel_err(to_np(gs), os_) <= TOL["f32"]
+
+
+def test_state_update_optional_inputs_absent(device):
+    """No D, no gate, no bias, softplus off, on an odd batch and a ragged dim."""
+    batch, dim, N = 3, 70, 16
+    rng = np.random.default_rng(4242)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    st = f(batch, dim, N)
+    u, Bv, Cv = f(batch, dim), f(batch, N), f(batch, N)
+    dl = np.abs(f(batch, dim)) * np.float32(0.05) + np.float32(1e-3)
+    A = si.s4d_real_A(dim, N)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    gs = T(st)
+    y = ss.selscan_state_update(gs, T(u), T(dl), T(A), T(Bv), T(Cv), None, None, None, False)
+    os_ = st.astype(np.float64)
+    ey = oracle.state_update(os_, u, dl, A, Bv, Cv, None, None, None, False)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(y), ey) <= TOL["f32"]
+    assert rel_err(to_np(gs), os_) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("dtype", [si.F32, si.BF16])
