@@ -111,6 +111,7 @@ def test_bwd_variants_every_state_size(device, N, dtype):
     check_bwd_ex(inp, device, 1423 + N, ZOH, None, what="N%d zoh" % N)
     check_bwd_ex(inp, device, 1424 + N, REV, conv_for("k1_bias", 96, 1425 + N),
                  what="N%d rev conv1" % N)
+    check_bwd_ex(inp, device, 1426 + N, 0, conv_for("k2", 96, 1427 + N), what="N%d conv2" % N)
 
 
 @pytest.mark.parametrize("flags", [ZOH, REV, ZOH | REV])
@@ -231,7 +232,7 @@ def test_bwd_variants_bitwise_repeatable(device):
             assert torch.equal(g1[k], g2[k]), k
 
 
-@pytest.mark.parametrize("flags", [REV, ZOH | REV])
+@pytest.mark.parametrize("flags", [0, REV, ZOH | REV])
 def test_bwd_variants_layer_workload(device, flags):
     """The 130M-layer shape (batch 8, L 2048, D 1536, N 16, bf16, gate, D,
     bias) with the conv prologue (k = 4, bias), every gradient in full."""
