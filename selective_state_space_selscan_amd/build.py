@@ -33,8 +33,20 @@ HIP_FLAGS = [
 ]
 
 
+# Units that take the longest to compile (the N = 64 and N = 32 variant
+# instantiations, the look-back plan, the default forward), started first so
+# that a parallel build does not end waiting on one of them.
+SLOW_UNITS = ("_n64", "fwd_lookback", "fwd_stream.hip", "_n32", "bwd_stream_zoh")
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    def rank(path):
+        name = os.path.basename(path)
+        for i, key in enumerate(SLOW_UNITS):
+            if key in name:
+                return (i, name)
+        return (len(SLOW_UNITS), name)
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")), key=rank)
 
 
 def _run(cmd, verbose):
