@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --pmc-run            # workload for rocprofv3 --pmc (see below)
+    python bench.py --pmc-run --pass bwd # the same for the backward
     python bench.py --parse-pmc FETCH_DIR WRITE_DIR   # -> profiles/traffic_<workload>.json
     python bench.py --pass bwd           # the backward (selscan_bwd) on the same workload
     python bench.py --variant zoh,rev,conv4   # forward variants through selscan_fwd_ex
@@ -176,12 +177,15 @@ def make_inputs(w, dev, rotate):
     return inp, sets
 
 
-def pmc_run(w, reps=3, warmup=200):
+def pmc_run(w, which="fwd", reps=3, warmup=200):
     """Workload for the counter runs: one plain 1 GiB device copy (the
-    calibration), ``warmup`` forward calls (the clocks ramp up), then ``reps``
-    forward calls, the ones the counters are read on."""
+    calibration), ``warmup`` calls (the clocks ramp up), then ``reps`` calls,
+    the ones the counters are read on: forward calls, or with ``which`` =
+    "bwd" backward calls as ``--pass bwd`` times them (dy seeded, no
+    dh_last, one workspace)."""
     import torch
 
+    import selscan_inputs as si
     import selective_state_space_selscan_amd as ss
     dev = torch.device("cuda:0")
     src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
@@ -192,11 +196,22 @@ def pmc_run(w, reps=3, warmup=200):
     del src, dst
     _, sets = make_inputs(w, dev, 1)
     t = sets[0]
-    for _ in range(warmup + reps):
-        ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
-                       t["delta_bias"], True, None, return_last_state=w.want_last_state)
+    if which == "bwd":
+        rng = np.random.default_rng([w.seed, 4242])
+        dy = torch.from_numpy(rng.standard_normal((w.batch, w.L, w.dim), dtype=np.float32))
+        dy = dy.to(dev).to(t["u"].dtype)
+        code = ss.SELSCAN_BF16 if w.dtype == si.BF16 else ss.SELSCAN_F32
+        ws = torch.empty(ss.selscan_bwd_workspace_bytes(w.batch, w.L, w.dim, w.N, code),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(warmup + reps):
+            ss.selscan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"], t["z"],
+                           t["delta_bias"], True, None, None, workspace=ws)
+    else:
+        for _ in range(warmup + reps):
+            ss.selscan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
+                           t["delta_bias"], True, None, return_last_state=w.want_last_state)
     torch.cuda.synchronize()
-    print("pmc-run done", w.name, warmup, reps, flush=True)
+    print("pmc-run done", w.name, which, warmup, reps, flush=True)
 
 
 def parse_pmc(w, fetch_dir, write_dir, reps=3):
@@ -414,11 +429,12 @@ def bwd_valu_slots(N, gate, es, flags=0, conv_k=0):
       Euler B_bar (plain, reverse):   recompute 3 (A_bar by the power chain,
         Delta u B, state FMA); adjoint step 11 (lambda, readout, A_bar h_{t-1},
         its product with lambda, the dDelta and dA sums, lambda.B, the dB and
-        dC terms, A_bar, the carry); the LDS sums of dB and dC 2  -> 16 N
+        dC terms, A_bar, the carry); the sums of dB and dC over the
+        wave's lanes 2 (their adds; the lane exchanges come on top) -> 16 N
       exact ZOH: recompute 14 (the coefficient (e - 1)/A with its series
         branch: 9, times u B: 2); adjoint 40 (the coefficient again, its
         derivative in A with its series branch: 13, and the extra terms of
-        dDelta and dA); the LDS sums 2                            -> 56 N
+        dDelta and dA); the lane sums 2                           -> 56 N
     Per element about 60 (softplus and sigmoid twice, SiLU and its derivative,
     widening, the per-element gradients and stores); the conv prologue adds
     48: the conv and SiLU of the scan input in the summary and checkpoint
@@ -622,7 +638,7 @@ def main():
         bench_decode(w, args.steps, args.warmup, args.ramp_ms)
         return
     if args.pmc_run:
-        pmc_run(w)
+        pmc_run(w, "bwd" if args.which == "bwd" else "fwd")
         return
     if args.torch_loop:
         print(json.dumps({"workload": w.name, **torch_loop_context(w)}), flush=True)

@@ -29,8 +29,8 @@
 //      TT states are recomputed from its checkpoint into registers, then the
 //      TT adjoint steps run.  Per-element gradients (du, ddelta, dz) are
 //      stored directly; dB_t, dC_t (sums over channels) are reduced over the
-//      wave's 64 lanes through LDS and written as one partial per channel
-//      group; dA, dD, dbias (sums over batch and time) as one partial per wave;
+//      wave's 64 lanes by a butterfly across the lanes (lanesum below) and
+//      written as one partial per channel group; dA, dD, dbias (sums over batch and time) as one partial per wave;
 //   5. a reduction of those partials.
 // Every reduction has a fixed order, so the result is bitwise repeatable.
 //
@@ -82,7 +82,6 @@ using stream::run_t_lo;
 using stream::scan_row;
 using stream::step_soff;
 
-constexpr int kLdsStride = kLanes + 1;  // padded rows: conflict-free LDS transposes
 constexpr int kHalo = kMaxConv - 1;     // conv window: steps before a step
 
 // Element type of the main pass's scan input and of its gradient: fp32 in
@@ -479,6 +478,112 @@ struct BwdAcc {
     float dD, dbias;
 };
 
+// ---------------------------------------------------------------------------
+// dB_t, dC_t: sums over the wave's 64 channels of each lane's 2N terms
+// ---------------------------------------------------------------------------
+// A butterfly across the lanes that halves the values per lane at each lane
+// bit, with no LDS: at bit 5 the pair (B term, C term) of one state, at bits
+// 4, 3, ... the partial sums of states that differ in bit 0, 1, ... of n.  At
+// each level a lane keeps one of two values and adds its partner lane's copy
+// of it, while sending the other one: lanes with the bit clear keep the
+// first.  gfx950's v_permlane32_swap and v_permlane16_swap exchange halves
+// and rows of two registers (bits 5 and 4); DPP reaches the lane 8 away
+// (row_ror:8, bit 3) and the mirrored lane of a half-row (bit 2) or quad
+// (bits 1 and 0), and a DPP move under a bank mask picks which of two values
+// a lane sends.  States arrive in order, so at most log2(G) partial sums wait
+// for their partner (G = min(N, 32) states per tree, N / G trees).  When a
+// tree is complete, lane l holds term (bit 5 of l ? C : B) of state
+// n(l) = bit 4 + 2 bit 3 + ... of l (log2 G bits), summed over the lanes
+// that agree with l in those bits; the lane bits below them are summed out
+// last, so that every lane holds a full sum over the 64 lanes.
+namespace lanesum {
+
+constexpr int kQuadIdentity = 0xE4, kQuadMirror = 0x1B, kQuadSwap = 0xB1;
+constexpr int kRowRor8 = 0x128, kRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// src in the lanes of the banks (groups of 4 lanes of a row) in BANKS, old elsewhere
+template <int BANKS>
+__device__ __forceinline__ float pick(float old, float src)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                      kQuadIdentity, 0xF, BANKS, false));
+}
+
+// Lanes with lane bit BIT clear: a(l) + a(partner); the others: b(l) + b(partner).
+template <int BIT>
+__device__ __forceinline__ float pair(float a, float b, int lane)
+{
+    if constexpr (BIT == 5 || BIT == 4) {
+        const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a),
+                                                                  __float_as_uint(b), false, false)
+                                : __builtin_amdgcn_permlane16_swap(__float_as_uint(a),
+                                                                  __float_as_uint(b), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (BIT == 3) {
+        return pick<0xC>(a, b) + dpp<kRowRor8>(pick<0xC>(b, a));
+    } else if constexpr (BIT == 2) {
+        return pick<0xA>(a, b) + dpp<kRowHalfMirror>(pick<0xA>(b, a));
+    } else {
+        const bool hi = ((lane >> BIT) & 1) != 0;
+        return (hi ? b : a) + dpp<BIT == 1 ? kQuadMirror : kQuadSwap>(hi ? a : b);
+    }
+}
+
+template <int N>
+struct Tree {
+    static constexpr int G = N < 32 ? N : 32;
+    static constexpr int LG = G == 4 ? 2 : G == 8 ? 3 : G == 16 ? 4 : 5;
+    static constexpr int TREES = N / G;
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "state size");
+    float pend[LG];
+    float out[TREES];
+
+    // Adds state n's terms; states come in increasing order.
+    __device__ __forceinline__ void add(int n, float tb, float tc, int lane)
+    {
+        float v = pair<5>(tb, tc, lane);
+#pragma unroll
+        for (int k = 0; k < LG; ++k) {
+            if (((n >> k) & 1) == 0) {
+                pend[k] = v;
+                return;
+            }
+            switch (k) {
+            case 0: v = pair<4>(pend[k], v, lane); break;
+            case 1: v = pair<3>(pend[k], v, lane); break;
+            case 2: v = pair<2>(pend[k], v, lane); break;
+            case 3: v = pair<1>(pend[k], v, lane); break;
+            default: v = pair<0>(pend[k], v, lane); break;
+            }
+        }
+        if (LG <= 2)
+            v += dpp<kRowHalfMirror>(v);
+        if (LG <= 3)
+            v += dpp<kQuadMirror>(v);
+        if (LG <= 4)
+            v += dpp<kQuadSwap>(v);
+        out[n / G] = v;
+    }
+    // The lanes that store a sum, the state of tree 0 and the term each holds.
+    __device__ static bool stores(int lane) { return (lane & ((1 << (5 - LG)) - 1)) == 0; }
+    __device__ static int state(int lane)
+    {
+        int n = 0;
+#pragma unroll
+        for (int k = 0; k < LG; ++k)
+            n |= ((lane >> (4 - k)) & 1) << k;
+        return n;
+    }
+    __device__ static bool is_c(int lane) { return (lane >> 5) != 0; }
+};
+
+}  // namespace lanesum
+
 // TT steps: states recomputed from the chunk's checkpoint, then the adjoint
 // steps from the last to the first.
 template <int N, bool POW, int VAR, typename TIO>
@@ -487,7 +592,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
                                           const float (&A2)[N], const float (&invA)[N],
                                           float (&g)[N], float (&dA)[N], BwdAcc &acc, bool gated,
                                           const BwdOut &o, int64_t grp_in_row, int64_t batch,
-                                          float *lds, int lane, bool active)
+                                          int lane, bool active)
 {
     constexpr bool ZOH = (VAR & kVarZoh) != 0;
     using TU = UType<VAR, TIO>;
@@ -554,8 +659,6 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
     const __amdgpu_buffer_rsrc_t rdz = make_rsrc(gated ? (TIO *)o.dz + elem : nullptr,
                                                  gated ? bytes : 0);
     const int voff_du = S == 1 ? c.voff_store : (active ? c.voff * S : stream::kStoreOffsetOutOfRange);
-    float *ldsB = lds;
-    float *ldsC = lds + N * kLdsStride;
 #pragma unroll
     for (int i = TT - 1; i >= 0; --i) {
         const bool valid = i < rows;
@@ -581,13 +684,14 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
         const float r = POW ? exp2_decay(dt * c.A2_0, tag<TIO>()) : 0.0f;
         float pw = 1.0f;
         float ypre = c.Dd * ut, sLB = 0.0f, wA = 0.0f, wE = 0.0f;
+        lanesum::Tree<N> sums;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             const float Bn = row_val<N>(brow, n), Cn = row_val<N>(crow, n);
             const float hn = hs[i][n];
             const float lam = fmaf(Cn, dypre, g[n]);
             ypre = fmaf(Cn, hn, ypre);
-            float a = 0.0f;
+            float a = 0.0f, tb;
             if constexpr (ZOH || !FIXED)
                 a = POW ? (pw *= r) : exp2_decay(dt * A2[n], tag<TIO>());
             if constexpr (ZOH) {
@@ -600,17 +704,17 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
                 wE = fmaf(a, lb, wE);
                 dA[n] = fmaf(dt, wq, fmaf(zoh_dcoeff(dt, x2, a, cn, invA[n]), lb * ut, dA[n]));
                 sLB = fmaf(cn, lb, sLB);
-                ldsB[n * kLdsStride + lane] = lam * (cn * ut_a);
+                tb = lam * (cn * ut_a);
             } else {
                 const float q = fmaf(-du, Bn, hn);        // A_bar_t h_{t-1}
                 const float wq = lam * q;
                 wA = fmaf(POW ? (float)(n + 1) : A2[n], wq, wA);
                 dA[n] = fmaf(dt, wq, dA[n]);
                 sLB = fmaf(lam, Bn, sLB);
-                ldsB[n * kLdsStride + lane] = lam * du_a;
+                tb = lam * du_a;
             }
-            // this lane's terms of dC_t[n]; row n of the LDS tiles
-            ldsC[n * kLdsStride + lane] = dypre_a * hn;
+            // this lane's terms of dB_t[n] and dC_t[n] into the lane sums
+            sums.add(n, tb, dypre_a * hn, lane);
             if constexpr (!ZOH && FIXED)
                 a = POW ? (pw *= r) : exp2_decay(dt * A2[n], tag<TIO>());
             g[n] = a * lam;
@@ -634,28 +738,15 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
             const float dz = dyt * ypre * sz * (1.0f + zt * (1.0f - sz));
             buf_store(rdz, c.voff_store, soff, dz, (TIO *)nullptr);
         }
-        // dB_t[n], dC_t[n] summed over the wave's 64 channels: 64/N lanes share
-        // row n, each adds N entries, then xor-shuffles combine the shares.
-        __syncthreads();
-        const int nl = lane % N, share = lane / N;
-        float sb = 0.0f, sc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            sb += ldsB[nl * kLdsStride + share * N + j];
-            sc += ldsC[nl * kLdsStride + share * N + j];
-        }
-#pragma unroll
-        for (int m = N; m < kLanes; m <<= 1) {
-            sb += __shfl_xor(sb, m);
-            sc += __shfl_xor(sc, m);
-        }
-        __syncthreads();
-        if (lane < N && valid) {
+        // dB_t[n], dC_t[n] summed over the wave's 64 channels
+        if (valid && lanesum::Tree<N>::stores(lane)) {
             const int64_t t = FIXED ? (REVF ? c.L - 1 - (t0 + i) : t0 + i)
                                     : row - c.bL;   // timestep of the step
-            const int64_t off = ((grp_in_row * batch + c.b) * c.L + t) * N + lane;
-            o.pB[off] = sb;
-            o.pC[off] = sc;
+            float *p = lanesum::Tree<N>::is_c(lane) ? o.pC : o.pB;
+            p += ((grp_in_row * batch + c.b) * c.L + t) * N + lanesum::Tree<N>::state(lane);
+#pragma unroll
+            for (int tr = 0; tr < lanesum::Tree<N>::TREES; ++tr)
+                p[tr * lanesum::Tree<N>::G] = sums.out[tr];
         }
     }
 }
@@ -667,7 +758,7 @@ __device__ __forceinline__ void bwd_part(const UType<VAR, TIO> *u, const TIO *de
                                          const float (&A2)[N], const float (&invA)[N],
                                          float (&g)[N], float (&dA)[N], BwdAcc &acc,
                                          const BwdOut &o, int64_t grp_in_row, int64_t batch,
-                                         float *lds, int lane, bool active)
+                                         int lane, bool active)
 {
     const bool gated = z != nullptr;
     const int64_t nchunks = (c.l_end - c.l_begin + TT - 1) / TT;
@@ -677,7 +768,7 @@ __device__ __forceinline__ void bwd_part(const UType<VAR, TIO> *u, const TIO *de
     for (;;) {
         load_bwd_chunk<VAR>(B, u, delta, z, dy, c, t0 - TT, true, c.l_begin);
         bwd_chunk<N, POW, VAR>(A, Bm, Cm, c, t0, ck + (t0 / TT) * (N * kLanes), A2, invA, g, dA,
-                               acc, gated, o, grp_in_row, batch, lds, lane, active);
+                               acc, gated, o, grp_in_row, batch, lane, active);
         t0 -= TT;
         if (t0 < c.l_begin)
             break;
@@ -699,7 +790,7 @@ constexpr int bwd_waves_per_eu()
     return 2;
 }
 
-// One wave per workgroup: the LDS transposes synchronise with __syncthreads.
+// One wave per workgroup.
 // u_in: the scan input, the I/O type or (kVarUf) fp32; o.du takes its
 // gradient in the same type and layout (with kVarUf, u and o.du may be one
 // buffer: a wave reads each element of its part before it stores there).
@@ -719,7 +810,6 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     constexpr bool ZOH = (VAR & kVarZoh) != 0;
     static_assert((VAR & kVarConv) == 0, "the main pass takes the conv prologue's output");
     const UType<VAR, TIO> *u = (const UType<VAR, TIO> *)u_in;
-    __shared__ float lds[2 * N * kLdsStride];
     WaveSetup w;
     if (!setup_wave(w, blockIdx.x, groups, parts, L, dim, part_len, (int)sizeof(TIO), rev))
         return;
@@ -751,10 +841,10 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     const float *ck = ckpt + w.grp * nck * (N * kLanes) + w.lane;
     if (pow_path)
         bwd_part<N, true, VAR>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir, batch,
-                               lds, w.lane, w.active);
+                               w.lane, w.active);
     else
         bwd_part<N, false, VAR>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir,
-                                batch, lds, w.lane, w.active);
+                                batch, w.lane, w.active);
     if (w.active) {
         const int64_t slot = c.b * parts + w.part;
 #pragma unroll

@@ -82,13 +82,15 @@ def test_forward_in_a_graph(device, monkeypatch, plan):
         torch.cuda.synchronize()
         if plan is None:
             assert torch.equal(gy, ey[0]) and torch.equal(gh, ey[1]), "replay %d" % k
-        else:
-            # the look-back plan's results may differ in rounding from call to
-            # call (a part uses an inclusive state or composes aggregates)
-            assert rel_err(to_np(gy), to_np(ey[0])) <= TOL["bf16"]
-        if k == 0:
-            oy, oh = oracle.fwd_inputs(inp)
-            assert rel_err(to_np(gy), oy) <= TOL["bf16"] and rel_err(to_np(gh), oh) <= TOL["bf16"]
+        if plan is None and k > 0:
+            continue
+        # the look-back plan's results may differ in rounding from call to
+        # call (a part uses an inclusive state or composes aggregates), so
+        # that two calls' bf16 outputs can differ by one unit in the last
+        # place: every replay is checked against the oracle instead
+        oy, oh = oracle.fwd_inputs(inp)
+        ry, rh = rel_err(to_np(gy), oy), rel_err(to_np(gh), oh)
+        assert ry <= TOL["bf16"] and rh <= TOL["bf16"], ("replay %d" % k, ry, rh)
 
 
 def test_backward_in_a_graph(device):
