@@ -481,24 +481,35 @@ struct BwdAcc {
 // ---------------------------------------------------------------------------
 // dB_t, dC_t: sums over the wave's 64 channels of each lane's 2N terms
 // ---------------------------------------------------------------------------
-// A butterfly across the lanes that halves the values per lane at each lane
-// bit, with no LDS: at bit 5 the pair (B term, C term) of one state, at bits
-// 4, 3, ... the partial sums of states that differ in bit 0, 1, ... of n.  At
-// each level a lane keeps one of two values and adds its partner lane's copy
-// of it, while sending the other one: lanes with the bit clear keep the
-// first.  gfx950's v_permlane32_swap and v_permlane16_swap exchange halves
-// and rows of two registers (bits 5 and 4); DPP reaches the lane 8 away
-// (row_ror:8, bit 3) and the mirrored lane of a half-row (bit 2) or quad
-// (bits 1 and 0), and a DPP move under a bank mask picks which of two values
-// a lane sends.  States arrive in order, so at most log2(G) partial sums wait
-// for their partner (G = min(N, 32) states per tree, N / G trees).  When a
-// tree is complete, lane l holds term (bit 5 of l ? C : B) of state
-// n(l) = bit 4 + 2 bit 3 + ... of l (log2 G bits), summed over the lanes
-// that agree with l in those bits; the lane bits below them are summed out
-// last, so that every lane holds a full sum over the 64 lanes.
+// A butterfly across the lanes that halves the values per lane at each
+// level, with no LDS.  A level pairs two values a and b with a lane mask m:
+// every lane l adds its partner l ^ m's copy of one of them, lanes with the
+// level's split bit clear keeping a, the others b.  The first level pairs
+// the B and the C term of a state, the next ones the partial sums of states
+// that differ in bit 0, 1, ... of n.  The levels go from the cheapest
+// exchange to the dearest, since each level has half the pairs of the one
+// before:
+//   lane ^ 8 (split bit 3): DPP row_ror:8; lane ^ 7 (bit 2): DPP
+//     row_half_mirror.  Two VALU ops: b + b(partner) in every lane, then a
+//     DPP add under a bank mask writes a + a(partner) into the lanes whose
+//     split bit is clear (the banks are the 4-lane groups of a row).
+//   lane ^ 32 (bit 5), lane ^ 16 (bit 4): gfx950's v_permlane32_swap and
+//     v_permlane16_swap exchange halves or rows of the two registers
+//     (two issue slots), one add.
+//   lane ^ 3 (bit 1), lane ^ 1 (bit 0): DPP quad_perm, a select on each
+//     side (three ops).
+// The masks 8, 7, 32, 16, 3, 1 are independent and no level flips an
+// earlier level's split bit, so partners always hold the same value and a
+// value's sum runs over all 64 lanes.  States arrive in order, so at most
+// log2(G) partial sums wait for their partner (G = min(N, 32) states per
+// tree, N / G trees).  Lane masks left over when G < 32 are summed out at
+// the end, so that every lane holds a full sum: lane l holds the C term if
+// bit 3 of l is set, else the B term, of state n(l) whose bits 0, 1, 2, 3, 4
+// are bits 2, 5, 4, 1, 0 of l (as many as the tree has); the lanes whose
+// left-over bits are clear store it.
 namespace lanesum {
 
-constexpr int kQuadIdentity = 0xE4, kQuadMirror = 0x1B, kQuadSwap = 0xB1;
+constexpr int kQuadMirror = 0x1B, kQuadSwap = 0xB1;
 constexpr int kRowRor8 = 0x128, kRowHalfMirror = 0x141;
 
 template <int CTRL>
@@ -506,33 +517,65 @@ __device__ __forceinline__ float dpp(float v)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// src in the lanes of the banks (groups of 4 lanes of a row) in BANKS, old elsewhere
-template <int BANKS>
-__device__ __forceinline__ float pick(float old, float src)
+
+// d, with a + a(l ^ 8) written into the lanes of banks 0 and 1 of each row
+// (lane bit 3 clear).  The DPP source may have been written by the VALU op
+// just before: two wait states first.
+__device__ __forceinline__ float add_xor8_into_low(float d, float a)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
-                                                      kQuadIdentity, 0xF, BANKS, false));
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3"
+        : "+v"(d) : "v"(a));
+    return d;
+}
+// d, with a + a(l ^ 7) written into the lanes of banks 0 and 2 (lane bit 2
+// clear); row_half_mirror takes lane 7 - i of each half row of 8.
+__device__ __forceinline__ float add_xor7_into_low(float d, float a)
+{
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5"
+        : "+v"(d) : "v"(a));
+    return d;
 }
 
-// Lanes with lane bit BIT clear: a(l) + a(partner); the others: b(l) + b(partner).
+// One level: lanes with lane bit BIT clear return a(l) + a(partner), the
+// others b(l) + b(partner).
 template <int BIT>
 __device__ __forceinline__ float pair(float a, float b, int lane)
 {
-    if constexpr (BIT == 5 || BIT == 4) {
+    // (b's product is not fused into the add: the add then takes b's DPP
+    // copy as its operand, one op)
+#pragma clang fp contract(off)
+    if constexpr (BIT == 3) {
+        return add_xor8_into_low(b + dpp<kRowRor8>(b), a);
+    } else if constexpr (BIT == 2) {
+        return add_xor7_into_low(b + dpp<kRowHalfMirror>(b), a);
+    } else if constexpr (BIT == 5 || BIT == 4) {
         const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a),
                                                                   __float_as_uint(b), false, false)
                                 : __builtin_amdgcn_permlane16_swap(__float_as_uint(a),
                                                                   __float_as_uint(b), false, false);
         return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    } else if constexpr (BIT == 3) {
-        return pick<0xC>(a, b) + dpp<kRowRor8>(pick<0xC>(b, a));
-    } else if constexpr (BIT == 2) {
-        return pick<0xA>(a, b) + dpp<kRowHalfMirror>(pick<0xA>(b, a));
     } else {
         const bool hi = ((lane >> BIT) & 1) != 0;
         return (hi ? b : a) + dpp<BIT == 1 ? kQuadMirror : kQuadSwap>(hi ? a : b);
     }
 }
+
+// v summed with its copy in lane l ^ (1 << BIT), for the left-over bits.
+template <int BIT>
+__device__ __forceinline__ float fold(float v)
+{
+    if constexpr (BIT == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        static_assert(BIT == 1 || BIT == 0, "left-over lane bits");
+        return v + dpp<BIT == 1 ? kQuadMirror : kQuadSwap>(v);
+    }
+}
+
+// The lane bit of each state bit of n (the B/C split is bit 3).
+constexpr int kStateBit[5] = {2, 5, 4, 1, 0};
 
 template <int N>
 struct Tree {
@@ -546,40 +589,47 @@ struct Tree {
     // Adds state n's terms; states come in increasing order.
     __device__ __forceinline__ void add(int n, float tb, float tc, int lane)
     {
-        float v = pair<5>(tb, tc, lane);
+        float v = pair<3>(tb, tc, lane);
 #pragma unroll
         for (int k = 0; k < LG; ++k) {
             if (((n >> k) & 1) == 0) {
                 pend[k] = v;
                 return;
             }
-            switch (k) {
-            case 0: v = pair<4>(pend[k], v, lane); break;
-            case 1: v = pair<3>(pend[k], v, lane); break;
+            switch (kStateBit[k]) {
             case 2: v = pair<2>(pend[k], v, lane); break;
-            case 3: v = pair<1>(pend[k], v, lane); break;
+            case 5: v = pair<5>(pend[k], v, lane); break;
+            case 4: v = pair<4>(pend[k], v, lane); break;
+            case 1: v = pair<1>(pend[k], v, lane); break;
             default: v = pair<0>(pend[k], v, lane); break;
             }
         }
-        if (LG <= 2)
-            v += dpp<kRowHalfMirror>(v);
-        if (LG <= 3)
-            v += dpp<kQuadMirror>(v);
-        if (LG <= 4)
-            v += dpp<kQuadSwap>(v);
+        if constexpr (LG <= 2)
+            v = fold<4>(v);
+        if constexpr (LG <= 3)
+            v = fold<1>(v);
+        if constexpr (LG <= 4)
+            v = fold<0>(v);
         out[n / G] = v;
     }
     // The lanes that store a sum, the state of tree 0 and the term each holds.
-    __device__ static bool stores(int lane) { return (lane & ((1 << (5 - LG)) - 1)) == 0; }
+    __device__ static bool stores(int lane)
+    {
+        int left = 0;
+#pragma unroll
+        for (int k = LG; k < 5; ++k)
+            left |= 1 << kStateBit[k];
+        return (lane & left) == 0;
+    }
     __device__ static int state(int lane)
     {
         int n = 0;
 #pragma unroll
         for (int k = 0; k < LG; ++k)
-            n |= ((lane >> (4 - k)) & 1) << k;
+            n |= ((lane >> kStateBit[k]) & 1) << k;
         return n;
     }
-    __device__ static bool is_c(int lane) { return (lane >> 5) != 0; }
+    __device__ static bool is_c(int lane) { return ((lane >> 3) & 1) != 0; }
 };
 
 }  // namespace lanesum
