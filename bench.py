@@ -421,7 +421,7 @@ def device_copy_gbps(dev, nbytes=1 << 29, reps=10):
     return 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
 
 
-def bwd_valu_slots(N, gate, es, flags=0, conv_k=0):
+def bwd_valu_slots(N, gate, es, flags=0, conv_k=0, general_a=False):
     """fp32 VALU slots per (b, l, d) element of the backward as built, counted
     from the inner loops of its main pass (the summary and checkpoint passes
     and the carries are extra work of the recomputation scheme, not counted;
@@ -431,6 +431,9 @@ def bwd_valu_slots(N, gate, es, flags=0, conv_k=0):
         its product with lambda, the dDelta and dA sums, lambda.B, the dB and
         dC terms, A_bar, the carry); the sums of dB and dC over the
         wave's lanes 2 (their adds; the lane exchanges come on top) -> 16 N
+      general A (Euler): A_bar = exp2(Delta A[d,n] log2 e) per state in the
+        recompute and in the adjoint step (a multiply and an exp2, 3 slots,
+        in place of the power chain's multiply)                   -> 20 N
       exact ZOH: recompute 14 (the coefficient (e - 1)/A with its series
         branch: 9, times u B: 2); adjoint 40 (the coefficient again, its
         derivative in A with its series branch: 13, and the extra terms of
@@ -442,7 +445,9 @@ def bwd_valu_slots(N, gate, es, flags=0, conv_k=0):
     and the epilogue's conv backward (28: the pre-activation again, its
     sigmoid, SiLU', the dconv_w and dconv_b sums and the transposed conv of
     dx)."""
-    per_n = 56 if flags & VARIANT_FLAGS["zoh"] else 16
+    if general_a:
+        assert not flags & VARIANT_FLAGS["zoh"], "general A with exact ZOH is not counted"
+    per_n = 56 if flags & VARIANT_FLAGS["zoh"] else (20 if general_a else 16)
     return per_n * N + 60 + (48 if conv_k else 0)
 
 
@@ -459,6 +464,9 @@ def bench_bwd(w, args):
     dev = torch.device("cuda:0")
     inp, sets = make_inputs(w, dev, 1)
     t = sets[0]
+    general_a = args.a_form == "general"
+    if general_a:
+        t["A"] = torch.from_numpy(si.perturbed_A(w.dim, w.N, w.seed)).to(dev)
     rng = np.random.default_rng([w.seed, 4242])
     dy = torch.from_numpy(rng.standard_normal((w.batch, w.L, w.dim), dtype=np.float32)).to(dev)
     dy = dy.to(t["u"].dtype)
@@ -498,8 +506,8 @@ def bench_bwd(w, args):
                                                              ramp_ms=args.ramp_ms)
     es = 2 if w.dtype == si.BF16 else 4
     elems = w.batch * w.L * w.dim
-    slots_el = bwd_valu_slots(w.N, w.gate, es, vflags, vconv) + (
-        algorithmic_valu_slots(w.N, w.gate, es) if pair else 0)
+    slots_el = bwd_valu_slots(w.N, w.gate, es, vflags, vconv, general_a) + (
+        algorithmic_valu_slots(w.N, w.gate, es, general_a) if pair else 0)
     slots = slots_el * elems
     # bytes the backward must move: the forward's inputs once, dy, and the
     # gradients du, ddelta, dz (dtype) and dB, dC (fp32) once
@@ -516,7 +524,8 @@ def bench_bwd(w, args):
         "dtype": "bf16" if w.dtype == si.BF16 else "f32", "data": "synthetic (seeded)",
         "config": {"workload": w.name, "pass": args.which, "batch": w.batch, "L": w.L,
                    "dim": w.dim,
-                   "N": w.N, "gate": w.gate},
+                   "N": w.N, "gate": w.gate,
+                   "abar": "exp2_per_state" if general_a else "power_chain_s4d_real"},
         "clock_ramp": {"calls": ramp[0], "ms": ramp[1]},
         "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms)),
                     "timed_quarters": quarters},

@@ -191,7 +191,10 @@ struct BwdChunk {
 
 // Loads the chunk at scan step t0.  Chunks past the part's end, or starting
 // below `lo` (the part's start), read nothing (zeros).
-template <int VAR, typename TIO, typename TU>
+// SCALAR_SOFF: the step offsets go through readfirstlane (they are wave-
+// uniform; where the compiler has them in VGPRs it would otherwise wrap
+// each load in a loop over the lanes' distinct offsets).
+template <int VAR, bool SCALAR_SOFF = false, typename TIO, typename TU>
 __device__ __forceinline__ void load_bwd_chunk(BwdChunk &ch, const TU *u, const TIO *delta,
                                                const TIO *z, const TIO *dy, const WaveCtx &c,
                                                int64_t t0, bool with_u, int64_t lo)
@@ -211,10 +214,15 @@ __device__ __forceinline__ void load_bwd_chunk(BwdChunk &ch, const TU *u, const 
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(z ? z + safe : nullptr, z ? bytes : 0);
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-        const int soff = step_soff<VAR>(c, i, (int)rows);
+        int soff = step_soff<VAR>(c, i, (int)rows);
+        int soff_u = widen_soff<S>(soff);
+        if constexpr (SCALAR_SOFF) {
+            soff = __builtin_amdgcn_readfirstlane(soff);
+            soff_u = __builtin_amdgcn_readfirstlane(soff_u);
+        }
         ch.x[i] = buf_load_raw(rx, c.voff, soff, delta);
         ch.dy[i] = buf_load_raw(ry, c.voff, soff, dy);
-        ch.u[i] = buf_load_raw(ru, c.voff * S, widen_soff<S>(soff), u);
+        ch.u[i] = buf_load_raw(ru, c.voff * S, soff_u, u);
         ch.z[i] = buf_load_raw(rz, c.voff, soff, z);
     }
 }
@@ -801,7 +809,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
     }
 }
 
-template <int N, bool POW, int VAR, typename TIO>
+template <int N, bool POW, int VAR, bool SCALAR_SOFF, typename TIO>
 __device__ __forceinline__ void bwd_part(const UType<VAR, TIO> *u, const TIO *delta,
                                          const TIO *z, const TIO *dy, const TIO *Bm,
                                          const TIO *Cm, const WaveCtx &c, const float *ck,
@@ -814,9 +822,9 @@ __device__ __forceinline__ void bwd_part(const UType<VAR, TIO> *u, const TIO *de
     const int64_t nchunks = (c.l_end - c.l_begin + TT - 1) / TT;
     int64_t t0 = c.l_begin + (nchunks - 1) * TT;
     BwdChunk A, B;
-    load_bwd_chunk<VAR>(A, u, delta, z, dy, c, t0, true, c.l_begin);
+    load_bwd_chunk<VAR, SCALAR_SOFF>(A, u, delta, z, dy, c, t0, true, c.l_begin);
     for (;;) {
-        load_bwd_chunk<VAR>(B, u, delta, z, dy, c, t0 - TT, true, c.l_begin);
+        load_bwd_chunk<VAR, SCALAR_SOFF>(B, u, delta, z, dy, c, t0 - TT, true, c.l_begin);
         bwd_chunk<N, POW, VAR>(A, Bm, Cm, c, t0, ck + (t0 / TT) * (N * kLanes), A2, invA, g, dA,
                                acc, gated, o, grp_in_row, batch, lane, active);
         t0 -= TT;
@@ -840,7 +848,17 @@ constexpr int bwd_waves_per_eu()
     return 2;
 }
 
-// One wave per workgroup.
+// One wave per workgroup.  Two launches over the same waves: the kernel
+// with both walks (APATH = kPathBoth, run_general = 0), in which the waves
+// whose channel group has structured A run the power-chain walk and the
+// others return, then the kernel with the exp2 walk alone (kPathGeneral),
+// in which those others run and the first ones return.  The exp2 walk
+// needs more registers than the power chain; sharing one allocation in the
+// first kernel it spilled to scratch (batch 8, L 2048, D 1536, N 16,
+// general A: main pass 569 us, against 359 us alone).  The power-chain
+// walk stays in the kernel with both, where it ran faster than compiled
+// alone (311 against 321 us): the walks are placed by one decision per
+// wave, so the run-time switch keeps its code as it was.
 // u_in: the scan input, the I/O type or (kVarUf) fp32; o.du takes its
 // gradient in the same type and layout (with kVarUf, u and o.du may be one
 // buffer: a wave reads each element of its part before it stores there).
@@ -848,14 +866,17 @@ constexpr int bwd_waves_per_eu()
 // the variant bits: such a name refers to the unnamed enum of those bits,
 // which the host and device compilations number differently, and the host
 // would then register a symbol that the device code does not define.
-template <int N, int VAR, typename TIO>
+constexpr int kPathBoth = 0, kPathGeneral = 2;
+
+template <int N, int VAR, typename TIO, int APATH>
 __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<N, VAR>()))) void bwd_main_kernel(
     const void *u_in, const TIO *__restrict__ delta, const TIO *__restrict__ z,
     const TIO *__restrict__ dy, const float *__restrict__ A, const TIO *__restrict__ Bm,
     const TIO *__restrict__ Cm, const float *__restrict__ D_skip,
     const float *__restrict__ delta_bias, int delta_softplus, const float *__restrict__ dh_last,
     const float *__restrict__ aentry, const float *__restrict__ ckpt, BwdOut o, int64_t L,
-    int64_t dim, int64_t batch, int64_t groups, int parts, int64_t part_len, int64_t nck, int rev)
+    int64_t dim, int64_t batch, int64_t groups, int parts, int64_t part_len, int64_t nck, int rev,
+    int run_general)
 {
     constexpr bool ZOH = (VAR & kVarZoh) != 0;
     static_assert((VAR & kVarConv) == 0, "the main pass takes the conv prologue's output");
@@ -867,6 +888,8 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     c.softplus = delta_softplus;
     float A2[N], invA[N];
     const bool pow_path = load_A<N, ZOH>(A, w.d, A2, invA, c);
+    if (APATH == kPathGeneral ? pow_path : !pow_path && !run_general)
+        return;   // the other launch's walk
     c.bias = delta_bias ? delta_bias[w.d] : 0.0f;
     c.Dd = D_skip ? D_skip[w.d] : 0.0f;
     // adjoint entering the part's last step from the right: dh_last folded
@@ -889,12 +912,12 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(bwd_wave
     const int64_t groups_per_row = (dim + kLanes - 1) / kLanes;
     const int64_t gir = w.grp % groups_per_row;
     const float *ck = ckpt + w.grp * nck * (N * kLanes) + w.lane;
-    if (pow_path)
-        bwd_part<N, true, VAR>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir, batch,
-                               w.lane, w.active);
+    if (APATH == kPathBoth && pow_path)
+        bwd_part<N, true, VAR, false>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir,
+                                      batch, w.lane, w.active);
     else
-        bwd_part<N, false, VAR>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g, dA, acc, o, gir,
-                                batch, w.lane, w.active);
+        bwd_part<N, false, VAR, APATH == kPathGeneral>(u, delta, z, dy, Bm, Cm, c, ck, A2, invA, g,
+                                                       dA, acc, o, gir, batch, w.lane, w.active);
     if (w.active) {
         const int64_t slot = c.b * parts + w.part;
 #pragma unroll
@@ -1145,24 +1168,38 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
             return err;
     }
     const int64_t waves = p.groups * p.parts;
-    auto main_pass = [&](auto kernel, auto u) {
+    auto launch_main = [&](auto kernel, auto u) {
         hipLaunchKernelGGL(kernel, dim3((unsigned)waves), dim3(kLanes), 0, s, u,
                            (const TIO *)a.fwd.delta, (const TIO *)a.fwd.z, (const TIO *)a.dy,
                            a.fwd.A, (const TIO *)a.fwd.Bm, (const TIO *)a.fwd.Cm, a.fwd.D_skip,
                            a.fwd.delta_bias, a.fwd.delta_softplus, a.dh_last,
                            (const float *)(split ? aentry : nullptr), ckpt, o, a.fwd.L,
-                           a.fwd.dim, a.fwd.batch, p.groups, p.parts, p.part_len, w.nck, x.rev);
+                           a.fwd.dim, a.fwd.batch, p.groups, p.parts, p.part_len, w.nck, x.rev,
+                           0);
         return hipGetLastError();
     };
+    // the power-chain waves in the kernel with both walks, then the others
+    // in the kernel with the exp2 walk alone
+    auto main_pass = [&](auto both_kernel, auto general_kernel, auto u) {
+        const hipError_t e = launch_main(both_kernel, u);
+        return e != hipSuccess ? e : launch_main(general_kernel, u);
+    };
     if constexpr (!CONV) {
-        err = main_pass(bwd_main_kernel<N, VAR, TIO>, (const TIO *)a.fwd.u);
+        err = main_pass(bwd_main_kernel<N, VAR, TIO, kPathBoth>,
+                        bwd_main_kernel<N, VAR, TIO, kPathGeneral>, (const TIO *)a.fwd.u);
     } else if constexpr ((VAR & kVarZoh) != 0) {
-        err = main_pass(bwd_main_kernel<N, (VAR & ~kVarConv) | kVarUf, TIO>, (const float *)uconv);
+        constexpr int V = (VAR & ~kVarConv) | kVarUf;
+        err = main_pass(bwd_main_kernel<N, V, TIO, kPathBoth>,
+                        bwd_main_kernel<N, V, TIO, kPathGeneral>, (const float *)uconv);
     } else {
         // Euler B_bar: the plain pass on fp32 inputs, direction fixed at
         // compile time
-        err = x.rev ? main_pass(bwd_main_kernel<N, kVarRev | kVarUf, TIO>, (const float *)uconv)
-                    : main_pass(bwd_main_kernel<N, kVarUf, TIO>, (const float *)uconv);
+        err = x.rev ? main_pass(bwd_main_kernel<N, kVarRev | kVarUf, TIO, kPathBoth>,
+                                bwd_main_kernel<N, kVarRev | kVarUf, TIO, kPathGeneral>,
+                                (const float *)uconv)
+                    : main_pass(bwd_main_kernel<N, kVarUf, TIO, kPathBoth>,
+                                bwd_main_kernel<N, kVarUf, TIO, kPathGeneral>,
+                                (const float *)uconv);
     }
     if (err != hipSuccess)
         return err;

@@ -47,3 +47,4 @@ def test_valu_slot_counts():
     assert bench.bwd_valu_slots(16, True, 2, flags=1) == 956
     assert bench.bwd_valu_slots(16, True, 2, flags=0, conv_k=4) == 364
     assert bench.bwd_valu_slots(16, True, 2, flags=3, conv_k=4) == 1004
+    assert bench.bwd_valu_slots(16, True, 2, general_a=True) == 380
