@@ -144,6 +144,20 @@ def perturbed_A(dim: int, N: int, seed: int, sigma: float = 0.25) -> np.ndarray:
     return (s4d_real_A(dim, N) * np.exp(eps)).astype(np.float32)
 
 
+def mixed_A(dim: int, N: int, seed: int) -> np.ndarray:
+    """S4D-real A on the even 64-channel groups and perturbed_A on the odd
+    ones, plus one perturbed channel in group 2 (when dim reaches it): a
+    call whose channel groups take both the power chain and the per-(t, n)
+    exponential, one group general through a single channel."""
+    A = s4d_real_A(dim, N)
+    pert = perturbed_A(dim, N, seed)
+    for g0 in range(64, dim, 128):
+        A[g0:g0 + 64] = pert[g0:g0 + 64]
+    if dim > 133:
+        A[133] = pert[133]
+    return A
+
+
 def make_fwd_inputs(batch: int, L: int, dim: int, N: int, dtype: str = BF16, gate: bool = True,
                     seed: int = BASE_SEED, delta_std: float = 0.5, D_value: Optional[float] = 1.0,
                     with_bias: bool = True, h0: bool = False) -> FwdInputs:

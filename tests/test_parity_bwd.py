@@ -96,6 +96,16 @@ def test_bwd_unstructured_A(device, N, L):
     check_bwd(inp, device, 1242 + N, "unstructured")
 
 
+@pytest.mark.parametrize("dtype", [si.F32, si.BF16])
+@pytest.mark.parametrize("N", [4, 16, 64])
+def test_bwd_mixed_structured_and_general_A(device, N, dtype):
+    """Channel groups with structured A and with general A in one call (the
+    main pass runs the first in one launch and the second in another)."""
+    inp = si.make_fwd_inputs(2, 700, 320, N, dtype, True, seed=1250 + N, h0=True)
+    inp.A = si.mixed_A(320, N, 1251 + N)
+    check_bwd(inp, device, 1252 + N, "mixed A N%d" % N)
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 64), (1, 2, 1), (3, 3, 100), (2, 5, 65),
                                    (1, 17, 130), (2, 2049, 64)])
 def test_bwd_ragged(device, shape):

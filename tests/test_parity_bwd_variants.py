@@ -125,6 +125,15 @@ def test_bwd_variants_unstructured_A(device, flags, N, L):
     check_bwd_ex(inp, device, 1442 + N, flags, si.conv_params(160, 3, 1443), what="unstructured")
 
 
+@pytest.mark.parametrize("flags", [ZOH, REV, ZOH | REV])
+def test_bwd_variants_mixed_structured_and_general_A(device, flags):
+    """Structured and general channel groups in one call, with the conv
+    prologue: both launches of the main pass on the variants."""
+    inp = si.make_fwd_inputs(2, 600, 320, 16, si.BF16, True, seed=1450, h0=True)
+    inp.A = si.mixed_A(320, 16, 1451)
+    check_bwd_ex(inp, device, 1452, flags, si.conv_params(320, 4, 1453), what="mixed A")
+
+
 def test_bwd_zoh_small_and_zero_A(device):
     """|Delta A| tiny (series branches everywhere) and A = 0 exactly
     (B_bar = Delta B, dc/dA = Delta^2 / 2), structured and not."""
