@@ -8,6 +8,7 @@
     python bench.py --variant zoh,rev,conv4   # forward variants through selscan_fwd_ex
     python bench.py --pass bwd --variant zoh,rev,conv4   # their backward (selscan_bwd_ex)
     python bench.py --pass fwdbwd        # forward + backward reusing its part state
+    python bench.py --pass fwdbwd --keep-checkpoints   # ... and its checkpoints
 
 One step = one selscan_fwd call over one batch of the workload.  The default
 workload is one Mamba-130M layer: batch 8, L 2048, D 1536, N 16, bf16 inputs,
@@ -482,17 +483,21 @@ def bench_bwd(w, args):
     pair = args.which == "fwdbwd"
     if pair and (vconv or vflags & ~ss.SELSCAN_FLAG_REVERSE):
         raise SystemExit("bench.py: --pass fwdbwd runs the plain path or 'rev' alone")
+    keep = bool(getattr(args, "keep_checkpoints", False))
+    if keep and (not pair or vflags):
+        raise SystemExit("bench.py: --keep-checkpoints goes with --pass fwdbwd, plain path")
+    kflag = ss.SELSCAN_FLAG_KEEP_CHECKPOINTS if keep else 0
     y = torch.empty_like(t["u"])
 
     def step(i):
         if pair:
             ss.selscan_fwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"], t["z"],
-                              t["delta_bias"], True, None, flags=vflags, y=y, workspace=ws,
-                              stream=stream)
+                              t["delta_bias"], True, None, flags=vflags | kflag, y=y,
+                              workspace=ws, stream=stream)
             ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"],
                               t["z"], t["delta_bias"], True, None, None,
-                              flags=vflags | ss.SELSCAN_FLAG_REUSE_FWD_STATE, workspace=ws,
-                              stream=stream)
+                              flags=vflags | ss.SELSCAN_FLAG_REUSE_FWD_STATE | kflag,
+                              workspace=ws, stream=stream)
             return
         if args.variant:
             ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["D_skip"],
@@ -525,7 +530,8 @@ def bench_bwd(w, args):
         "config": {"workload": w.name, "pass": args.which, "batch": w.batch, "L": w.L,
                    "dim": w.dim,
                    "N": w.N, "gate": w.gate,
-                   "abar": "exp2_per_state" if general_a else "power_chain_s4d_real"},
+                   "abar": "exp2_per_state" if general_a else "power_chain_s4d_real",
+                   "keep_checkpoints": keep},
         "clock_ramp": {"calls": ramp[0], "ms": ramp[1]},
         "call_ms": {"mean": call_mean, "single_call_p50": float(np.median(call_ms)),
                     "timed_quarters": quarters},
@@ -629,6 +635,9 @@ def main():
                     help="context only: time a plain PyTorch loop over timesteps against "
                          "selscan_fwd on the workload, print one JSON line")
     ap.add_argument("--variant", default="", help="variants: zoh, rev, convK (fwd or bwd)")
+    ap.add_argument("--keep-checkpoints", action="store_true",
+                    help="--pass fwdbwd: the forward keeps the backward's checkpoints "
+                         "(SELSCAN_FLAG_KEEP_CHECKPOINTS), the backward skips its checkpoint pass")
     ap.add_argument("--a", dest="a_form", choices=("s4d", "general"), default="s4d",
                     help="A = -(n+1) (S4D-real: the power-chain A_bar) or a perturbed, "
                          "general A (A_bar by one exp2 per (t, n))")

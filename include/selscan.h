@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 7
+#define SELSCAN_ABI_VERSION 8
 
 enum selscan_dtype {
     SELSCAN_F32 = 0,
@@ -224,12 +224,14 @@ int selscan_fwd_noalloc(const void *u, const void *delta, const float *A,
 #define SELSCAN_FLAG_ZOH_EXACT 1   /* B_bar = (exp(Delta A) - 1) / A * B, Delta B where A = 0 */
 #define SELSCAN_FLAG_REVERSE   2   /* scan from t = L-1 down to t = 0                      */
 #define SELSCAN_FLAG_REUSE_FWD_STATE 4   /* selscan_bwd_ex only: see there                 */
+#define SELSCAN_FLAG_KEEP_CHECKPOINTS 8  /* selscan_fwd_ex, then selscan_bwd_ex: see there */
 #define SELSCAN_MAX_CONV_WIDTH 4
 
 /*
  * Selective-scan forward with variants.  Arguments as selscan_fwd, plus:
  *
- *   flags        0 or an OR of SELSCAN_FLAG_ZOH_EXACT, SELSCAN_FLAG_REVERSE.
+ *   flags        0 or an OR of SELSCAN_FLAG_ZOH_EXACT, SELSCAN_FLAG_REVERSE; or
+ *                SELSCAN_FLAG_KEEP_CHECKPOINTS alone (below).
  *                ZOH_EXACT: the state update is
  *                  h = exp(Delta A) h + (exp(Delta A) - 1) / A * B u
  *                instead of h = exp(Delta A) h + Delta B u (the limit Delta B u
@@ -251,6 +253,17 @@ int selscan_fwd_noalloc(const void *u, const void *delta, const float *A,
  *
  * With flags = 0 and conv_width = 0 this is the default forward itself (the
  * results of selscan_fwd bit for bit).
+ *
+ * SELSCAN_FLAG_KEEP_CHECKPOINTS (alone: with another flag bit or
+ * conv_width > 0, SELSCAN_ERR_UNSUPPORTED): the forward of a training step
+ * whose backward reuses this workspace (selscan_bwd_ex with
+ * SELSCAN_FLAG_REUSE_FWD_STATE | SELSCAN_FLAG_KEEP_CHECKPOINTS).  The main
+ * pass also stores the state entering every 4-step chunk, the checkpoints
+ * that backward's recomputation would otherwise walk the sequence for: 4 N
+ * bytes per element (the paper walkthrough (m.lqnn.cn) §5.4: with memory to
+ * spare, recompute less).  The workspace must then hold
+ * selscan_bwd_workspace_bytes (SELSCAN_ERR_WORKSPACE otherwise).  y and
+ * h_last are bit for bit those of the call without the flag.
  *
  * Workspace: the same size as selscan_fwd (selscan_fwd_workspace_bytes).
  * Errors as selscan_fwd, and: SELSCAN_ERR_UNSUPPORTED for an unknown flag bit
@@ -358,6 +371,14 @@ int selscan_bwd(const void *u, const void *delta, const float *A,
  * The result is bit for bit that of the call without the flag.  The library
  * cannot check the correspondence: it is the caller's to keep.  A workspace
  * of selscan_bwd_workspace_bytes is large enough for the forward too.
+ *
+ * SELSCAN_FLAG_KEEP_CHECKPOINTS (with SELSCAN_FLAG_REUSE_FWD_STATE and no
+ * other flag bit, conv_width = 0; SELSCAN_ERR_UNSUPPORTED otherwise): that
+ * forward was the plain one run with SELSCAN_FLAG_KEEP_CHECKPOINTS, and the
+ * workspace also holds its checkpoint states; the backward reads them and
+ * skips its own checkpoint pass (and the forward entry states it needs).
+ * The gradients are within rounding of the call without the flag (the
+ * forward's states where the checkpoint pass would recompute them).
  */
 int selscan_bwd_ex(const void *u, const void *delta, const float *A,
                    const void *Bm, const void *Cm, const float *D_skip,

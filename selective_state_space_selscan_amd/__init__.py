@@ -18,6 +18,7 @@ from ._abi import (  # noqa: F401
     SELSCAN_BF16,
     SELSCAN_F32,
     SELSCAN_FLAG_REUSE_FWD_STATE,
+    SELSCAN_FLAG_KEEP_CHECKPOINTS,
     SELSCAN_FLAG_REVERSE,
     SELSCAN_FLAG_ZOH_EXACT,
     SELSCAN_MAX_CONV_WIDTH,

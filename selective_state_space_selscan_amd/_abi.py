@@ -17,6 +17,7 @@ SELSCAN_BF16 = 1
 SELSCAN_FLAG_ZOH_EXACT = 1
 SELSCAN_FLAG_REVERSE = 2
 SELSCAN_FLAG_REUSE_FWD_STATE = 4
+SELSCAN_FLAG_KEEP_CHECKPOINTS = 8
 SELSCAN_MAX_CONV_WIDTH = 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -198,9 +199,12 @@ def selscan_fwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: to
                    workspace: Optional[torch.Tensor] = None,
                    stream: Optional[torch.cuda.Stream] = None):
     """Forward with variants through ``selscan_fwd_ex``: ``flags`` is an OR of
-    SELSCAN_FLAG_ZOH_EXACT and SELSCAN_FLAG_REVERSE; ``conv_weight`` (dim, k)
-    float32 with k <= 4 (and ``conv_bias`` (dim,)) enables the causal conv1d +
-    SiLU prologue on u.  Other arguments and the result as ``selscan_fwd``."""
+    SELSCAN_FLAG_ZOH_EXACT and SELSCAN_FLAG_REVERSE, or
+    SELSCAN_FLAG_KEEP_CHECKPOINTS alone (the backward's checkpoints kept in
+    ``workspace``, which must then be given, of at least
+    selscan_bwd_workspace_bytes); ``conv_weight`` (dim, k) float32 with k <= 4
+    (and ``conv_bias`` (dim,)) enables the causal conv1d + SiLU prologue on u.
+    Other arguments and the result as ``selscan_fwd``."""
     return _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0,
                 return_last_state, y, h_last, workspace, stream,
                 (int(flags), conv_weight, conv_bias))
@@ -232,6 +236,12 @@ def _fwd(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, return_
     elif h_last is not None:
         h_last = _check_out(h_last, torch.float32, dev, "h_last", (batch, dim, N))
     ws_bytes = int(L_.selscan_fwd_workspace_bytes(batch, L, dim, N, code))
+    if ex is not None and ex[0] & SELSCAN_FLAG_KEEP_CHECKPOINTS:
+        # the checkpoints are for a later backward: they go to the caller's workspace
+        ws_bytes = int(L_.selscan_bwd_workspace_bytes(batch, L, dim, N, code))
+        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError("SELSCAN_FLAG_KEEP_CHECKPOINTS needs a workspace of at least "
+                             "selscan_bwd_workspace_bytes (%d)" % ws_bytes)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_ptr = _ptr(workspace) if ws_bytes else None
@@ -298,7 +308,11 @@ def selscan_bwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: to
     or ``selscan_fwd_ex`` with the same REVERSE flag) last ran in, on the
     same inputs, h0 and sizes, at least ``selscan_bwd_workspace_bytes``
     long; the backward then reads that forward's part summaries and entry
-    states instead of recomputing them (same result, bit for bit)."""
+    states instead of recomputing them (same result, bit for bit).  With
+    SELSCAN_FLAG_KEEP_CHECKPOINTS as well (plain only), that forward was
+    ``selscan_fwd_ex`` with SELSCAN_FLAG_KEEP_CHECKPOINTS, and its kept
+    checkpoint states replace the backward's checkpoint pass (the same
+    gradients up to rounding)."""
     return _bwd(u, delta, A, Bm, Cm, dy, D_skip, z, delta_bias, delta_softplus, h0, dh_last,
                 workspace, stream, (int(flags), conv_weight, conv_bias))
 

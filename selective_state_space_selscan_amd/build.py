@@ -34,9 +34,11 @@ HIP_FLAGS = [
 
 
 # Units that take the longest to compile (the N = 64 and N = 32 variant
-# instantiations, the look-back plan, the default forward), started first so
+# instantiations, the look-back plan, the default forward and its
+# checkpoint-keeping twin), started first so
 # that a parallel build does not end waiting on one of them.
-SLOW_UNITS = ("_n64", "fwd_lookback", "fwd_stream.hip", "_n32", "bwd_stream_zoh")
+SLOW_UNITS = ("_n64", "fwd_lookback", "fwd_stream.hip", "fwd_stream_keep", "_n32",
+              "bwd_stream_zoh")
 
 
 def sources():

@@ -152,6 +152,11 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N)
     return bwd::bwd_layout(batch, L, dim, N).total;
 }
 
+size_t bwd_checkpoint_offset(int64_t batch, int64_t L, int64_t dim, int64_t N)
+{
+    return bwd::bwd_layout(batch, L, dim, N).ckpt;
+}
+
 hipError_t launch_bwd_euler(const BwdArgs &a, const FwdExt &e, hipStream_t stream)
 {
     return bwd::launch_bwd_var<0>(a, e, stream);

@@ -1104,7 +1104,7 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
     o.pA = (float *)(base + w.pA); o.pD = (float *)(base + w.pD);
     o.pbias = (float *)(base + w.pbias);
     o.dh0 = a.dh0;
-    ExtParams x;
+    ExtParams x{};
     x.conv_w = CONV ? e.conv_w : nullptr;
     x.conv_b = CONV ? e.conv_b : nullptr;
     x.conv_k = CONV ? e.conv_k : 0;
@@ -1149,13 +1149,24 @@ hipError_t launch_bwd_n(const BwdArgs &a, const FwdExt &e, hipStream_t s)
                                         a.fwd.dim, N, p.parts, 1, cscr, s)
                      : hipSuccess;
     };
+    // the forward kept the checkpoints (the plain forward with
+    // kFwdFlagKeepCheckpoints, read with its part state): the adjoint
+    // summaries alone, and no forward entry states
+    const bool kept = (e.flags & kFwdFlagKeepCheckpoints) != 0;
     if constexpr ((VAR & kVarZoh) == 0) {
-        // the checkpoints need the forward entry states
-        if ((err = carry_fwd()) != hipSuccess)
-            return err;
-        pass23(bwd_pass23_kernel<N, VAR, 3, TIO>, adj_blocks, ck_blocks);
-        if ((err = hipGetLastError()) != hipSuccess || (err = carry_adj()) != hipSuccess)
-            return err;
+        if (kept) {
+            if (adj_blocks > 0)
+                pass23(bwd_pass23_kernel<N, VAR, 1, TIO>, adj_blocks, 0);
+            if ((err = hipGetLastError()) != hipSuccess || (err = carry_adj()) != hipSuccess)
+                return err;
+        } else {
+            // the checkpoints need the forward entry states
+            if ((err = carry_fwd()) != hipSuccess)
+                return err;
+            pass23(bwd_pass23_kernel<N, VAR, 3, TIO>, adj_blocks, ck_blocks);
+            if ((err = hipGetLastError()) != hipSuccess || (err = carry_adj()) != hipSuccess)
+                return err;
+        }
     } else {
         // checkpoints last, just before the main pass that reads them
         if (adj_blocks > 0)

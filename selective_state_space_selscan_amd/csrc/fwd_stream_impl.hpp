@@ -72,7 +72,10 @@ static_assert(TT <= kStreamTT, "plan rounds parts to kStreamTT steps");
 // the reverse-only call then compiles to the default's code with the
 // addressing mirrored.  kVarUf (backward only): the scan input is fp32 bits
 // whatever the I/O type (the conv prologue's output, computed beforehand).
-enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4, kVarRev = 8, kVarUf = 16 };
+// kVarKeep (the default forward's main pass only): the pass also stores the
+// state entering every TT-step chunk, the checkpoints a backward that reuses
+// this forward's workspace would otherwise recompute.
+enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4, kVarRev = 8, kVarUf = 16, kVarKeep = 32 };
 constexpr int kMaxConv = 4;
 
 // Variant arguments of the kernel (ignored when VAR = 0).
@@ -81,6 +84,8 @@ struct ExtParams {
     const float *conv_b;   // (dim), or null
     int conv_k;
     int rev;
+    float *ckpt;           // kVarKeep: (groups, nck, N, 64) states entering each chunk
+    int64_t nck;           // chunks per channel group: ceil(L / TT)
 };
 
 template <int TTc>
@@ -364,23 +369,36 @@ __device__ __forceinline__ void run_any_chunk(const Chunk &ch, const TIO *Bm, co
 }
 
 // Forward walk over the part (main pass, and the summary for general A).
+// kVarKeep: ck is this wave's lane of its channel group's checkpoints, and
+// the state entering each chunk is stored there first (every lane, those past
+// dim too: their values are finite and a reader may combine them with zeros).
 template <int N, bool SUMMARY, bool GATED, bool SOFTPLUS, bool POW, int VAR, typename TIO>
 __device__ __forceinline__ void run_part(const TIO *u, const TIO *delta, const TIO *z, TIO *y,
                                          const TIO *Bm, const TIO *Cm, const WaveCtx &c,
                                          const float (&A2)[N], const float (&invA)[N],
-                                         float (&h)[N], float &sdelta, float (&win)[kMaxConv - 1])
+                                         float (&h)[N], float &sdelta, float (&win)[kMaxConv - 1],
+                                         float *ck = nullptr)
 {
+    auto keep = [&](int64_t t) {
+        if constexpr ((VAR & kVarKeep) != 0 && !SUMMARY) {
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                ck[(t / TT) * (N * kLanes) + n * kLanes] = h[n];
+        }
+    };
     Chunk A, B;
     int64_t t0 = c.l_begin;
     load_chunk<GATED, VAR>(A, u, delta, z, c, t0);
     for (;;) {
         load_chunk<GATED, VAR>(B, u, delta, z, c, t0 + TT);
+        keep(t0);
         run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, VAR>(A, Bm, Cm, y, c, t0, A2, invA, h,
                                                              sdelta, win);
         t0 += TT;
         if (t0 >= c.l_end)
             break;
         load_chunk<GATED, VAR>(A, u, delta, z, c, t0 + TT);
+        keep(t0);
         run_any_chunk<N, SUMMARY, GATED, SOFTPLUS, POW, VAR>(B, Bm, Cm, y, c, t0, A2, invA, h,
                                                              sdelta, win);
         t0 += TT;
@@ -716,8 +734,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<N, VAR>()))) void fwd_stream_ker
 
     float sdelta = 0.0f;
     const bool gated = !SUMMARY && z != nullptr;
+    float *ck = nullptr;
+    if constexpr ((VAR & kVarKeep) != 0 && !SUMMARY)
+        ck = ext.ckpt + grp * ext.nck * (N * kLanes) + lane;
 #define SELSCAN_RUN(G, SP, PW)                                                                    \
-    run_part<N, SUMMARY, G, SP, PW, VAR>(u, delta, z, y, Bm, Cm, c, A2, invA, h, sdelta, win)
+    run_part<N, SUMMARY, G, SP, PW, VAR>(u, delta, z, y, Bm, Cm, c, A2, invA, h, sdelta, win, ck)
     if (SUMMARY && pow_path) {
         if (EXT || delta_softplus)
             summary_part_rev<N, true, VAR>(u, delta, Bm, c, win, h, sdelta);
@@ -780,7 +801,7 @@ hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p,
 {
     if (p.parts > 1) {
         const int64_t waves = p.groups * (p.parts - 1);
-        hipLaunchKernelGGL((fwd_stream_kernel<N, true, VAR, TIO>),
+        hipLaunchKernelGGL((fwd_stream_kernel<N, true, VAR & ~kVarKeep, TIO>),
                            dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                            dim3(kLanes * kWavesPerBlock), 0, s, (const TIO *)a.u,
                            (const TIO *)a.delta, (const TIO *)nullptr, (TIO *)nullptr, a.A,
@@ -810,7 +831,7 @@ hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p,
                        a.delta_softplus, a.h0, a.h_last, summ,                                    \
                        (const float *)(p.parts > kFoldInKernelMaxParts ? entry : nullptr), a.L,   \
                        a.dim, p.groups, p.parts, p.part_len, ext)
-    if constexpr (VAR == 0 || VAR == kVarRev) {
+    if constexpr ((VAR & ~kVarKeep) == 0 || VAR == kVarRev) {
         const int fx = 1 + (a.z ? 2 : 0) + (a.delta_softplus ? 1 : 0);
         if (fx == 4) SELSCAN_MAIN(4); else if (fx == 3) SELSCAN_MAIN(3);
         else if (fx == 2) SELSCAN_MAIN(2); else SELSCAN_MAIN(1);
@@ -829,7 +850,7 @@ hipError_t launch_ext_summaries(const FwdArgs &a, const FwdExt &e, const StreamP
     const int64_t waves = p.groups * (p.parts - 1);
     if (waves <= 0)
         return hipSuccess;
-    ExtParams x;
+    ExtParams x{};
     x.conv_w = e.conv_k > 0 ? e.conv_w : nullptr;
     x.conv_b = e.conv_k > 0 ? e.conv_b : nullptr;
     x.conv_k = e.conv_k;
@@ -892,7 +913,7 @@ hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
     const int occupancy = e.conv_k > 0 ? waves_per_eu<N, V0 | kVarConv>() : waves_per_eu<N, V0>();
     const StreamPlan p = make_stream_plan(a.batch, a.L, a.dim, occupancy);
     float *entry = entry_buffer(a.workspace, p, N);
-    ExtParams x;
+    ExtParams x{};
     x.conv_w = e.conv_k > 0 ? e.conv_w : nullptr;
     x.conv_b = e.conv_k > 0 ? e.conv_b : nullptr;
     x.conv_k = e.conv_k;

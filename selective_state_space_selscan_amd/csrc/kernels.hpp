@@ -87,6 +87,10 @@ hipError_t launch_fwd_lookback(const FwdArgs &a, int spin_limit, hipStream_t str
 constexpr int kFwdFlagZohExact = 1;
 constexpr int kFwdFlagReverse = 2;
 constexpr int kBwdFlagReuseFwdState = 4;   // backward: the workspace holds the forward's part state
+// forward: the main pass also stores the backward's checkpoints (the state
+// entering every 4-step chunk) in the workspace, at the backward layout's
+// offset; backward (with kBwdFlagReuseFwdState): they are there.
+constexpr int kFwdFlagKeepCheckpoints = 8;
 struct FwdExt {
     int flags;            // kFwdFlagZohExact | kFwdFlagReverse
     const float *conv_w;  // (dim, conv_k) when conv_k > 0
@@ -94,6 +98,12 @@ struct FwdExt {
     int conv_k;           // 0 = no conv prologue, else 1..4
 };
 hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream);
+// The default forward with kFwdFlagKeepCheckpoints (fwd_stream_keep.hip); its
+// workspace is a backward's (bwd_workspace_bytes).
+hipError_t launch_fwd_stream_keep(const FwdArgs &a, hipStream_t stream);
+// Byte offset of the checkpoint buffer in the backward's workspace layout,
+// from the workspace aligned up to 256 bytes.
+size_t bwd_checkpoint_offset(int64_t batch, int64_t L, int64_t dim, int64_t N);
 // One translation unit per (N, B_bar form): fwd_stream_ext_n<N>[_zoh].hip.
 #define SELSCAN_DECLARE_EXT(NN)                                                                   \
     hipError_t launch_fwd_stream_ext_n##NN(const FwdArgs &a, const FwdExt &e, hipStream_t s);    \

@@ -149,11 +149,14 @@ hipError_t scratch_ptr(void **out)
 // selscan_fwd_noalloc, whose workspace is the device's fixed scratch: there
 // a shape needing more than SELSCAN_NOALLOC_SCRATCH_BYTES is refused, and
 // the scratch is looked up only after every argument check has passed.
+// need_at_least: a larger workspace the call needs (selscan_fwd_ex keeping
+// the backward's checkpoints needs a backward's).
 int fwd_common(const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
                const float *D_skip, const void *z, const float *delta_bias, int delta_softplus,
                const float *h0, void *y, float *h_last, int64_t batch, int64_t L, int64_t dim,
                int64_t N, int dtype, const selscan::FwdExt *ext, void *workspace,
-               size_t workspace_bytes, void *stream, bool use_scratch = false)
+               size_t workspace_bytes, void *stream, bool use_scratch = false,
+               size_t need_at_least = 0)
 {
     if (dtype != SELSCAN_F32 && dtype != SELSCAN_BF16)
         return SELSCAN_ERR_DTYPE;
@@ -176,7 +179,8 @@ int fwd_common(const void *u, const void *delta, const float *A, const void *Bm,
     for (const void *p : all)
         if (p && !aligned16(p))
             return SELSCAN_ERR_UNSUPPORTED;
-    const size_t need = selscan_fwd_workspace_bytes(batch, L, dim, N, dtype);
+    size_t need = selscan_fwd_workspace_bytes(batch, L, dim, N, dtype);
+    need = need > need_at_least ? need : need_at_least;
     if (use_scratch) {
         if (need > (size_t)SELSCAN_NOALLOC_SCRATCH_BYTES)
             return SELSCAN_ERR_TOO_LARGE;
@@ -388,20 +392,30 @@ int selscan_fwd_ex(const void *u, const void *delta, const float *A, const void 
                    const float *conv_weight, const float *conv_bias, int64_t conv_width,
                    void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE))
+    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_KEEP_CHECKPOINTS))
         return SELSCAN_ERR_UNSUPPORTED;
     if (conv_width < 0)
         return SELSCAN_ERR_SHAPE;
     if (conv_width > SELSCAN_MAX_CONV_WIDTH)
         return SELSCAN_ERR_UNSUPPORTED;
+    // the checkpoints are kept by the plain forward alone
+    const bool keep = (flags & SELSCAN_FLAG_KEEP_CHECKPOINTS) != 0;
+    if (keep && (flags != SELSCAN_FLAG_KEEP_CHECKPOINTS || conv_width > 0))
+        return SELSCAN_ERR_UNSUPPORTED;
     selscan::FwdExt e;
     e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |
-              (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0);
+              (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0) |
+              (keep ? selscan::kFwdFlagKeepCheckpoints : 0);
     e.conv_w = conv_weight;
     e.conv_b = conv_bias;
     e.conv_k = (int)conv_width;
+    // with the checkpoints kept, the workspace is a backward's (a shape the
+    // backward refuses has no such size: the argument checks then name the
+    // error, or the workspace check fails, before any launch)
+    const size_t need = keep ? selscan_bwd_workspace_bytes(batch, L, dim, N, dtype) : 0;
     return fwd_common(u, delta, A, Bm, Cm, D_skip, z, delta_bias, delta_softplus, h0, y, h_last,
-                      batch, L, dim, N, dtype, &e, workspace, workspace_bytes, stream);
+                      batch, L, dim, N, dtype, &e, workspace, workspace_bytes, stream, false,
+                      keep && need == 0 ? (size_t)-1 : need);
 }
 
 size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype)
@@ -434,7 +448,12 @@ int selscan_bwd_ex(const void *u, const void *delta, const float *A, const void 
                    float *dconv_bias, int64_t batch, int64_t L, int64_t dim, int64_t N, int dtype,
                    void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_REUSE_FWD_STATE))
+    if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_REUSE_FWD_STATE |
+                  SELSCAN_FLAG_KEEP_CHECKPOINTS))
+        return SELSCAN_ERR_UNSUPPORTED;
+    // kept checkpoints come from the plain forward, read with its part state
+    if ((flags & SELSCAN_FLAG_KEEP_CHECKPOINTS) &&
+        flags != (SELSCAN_FLAG_KEEP_CHECKPOINTS | SELSCAN_FLAG_REUSE_FWD_STATE))
         return SELSCAN_ERR_UNSUPPORTED;
     if (conv_width < 0)
         return SELSCAN_ERR_SHAPE;
@@ -451,7 +470,8 @@ int selscan_bwd_ex(const void *u, const void *delta, const float *A, const void 
     selscan::FwdExt e;
     e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |
               (flags & SELSCAN_FLAG_REVERSE ? selscan::kFwdFlagReverse : 0) |
-              (flags & SELSCAN_FLAG_REUSE_FWD_STATE ? selscan::kBwdFlagReuseFwdState : 0);
+              (flags & SELSCAN_FLAG_REUSE_FWD_STATE ? selscan::kBwdFlagReuseFwdState : 0) |
+              (flags & SELSCAN_FLAG_KEEP_CHECKPOINTS ? selscan::kFwdFlagKeepCheckpoints : 0);
     e.conv_w = conv_weight;
     e.conv_b = conv_bias;
     e.conv_k = (int)conv_width;

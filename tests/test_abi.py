@@ -156,6 +156,11 @@ def fwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, **kw):
 
 INVALID_FWD_EX = [
     ("unknown_flag", dict(flags=4), ERR_UNSUP),
+    ("unknown_flag_16", dict(flags=16), ERR_UNSUP),
+    # the plain forward alone keeps the backward's checkpoints
+    ("keep_with_reverse", dict(flags=8 | 2), ERR_UNSUP),
+    ("keep_with_zoh", dict(flags=8 | 1), ERR_UNSUP),
+    ("keep_with_conv", dict(flags=8, conv_width=4, conv_w=fake(13)), ERR_UNSUP),
     ("negative_flag", dict(flags=-1), ERR_UNSUP),
     ("conv_width_5", dict(conv_width=5, conv_w=fake(13)), ERR_UNSUP),
     ("conv_width_neg", dict(conv_width=-1, conv_w=fake(13)), ERR_SHAPE),
@@ -253,7 +258,13 @@ def bwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, dconv_w=None, d
 
 
 INVALID_BWD_EX = [
-    ("unknown_flag", dict(flags=8), ERR_UNSUP),
+    ("unknown_flag", dict(flags=16), ERR_UNSUP),
+    # kept checkpoints are read with the plain forward's part state only
+    ("keep_without_reuse", dict(flags=8), ERR_UNSUP),
+    ("keep_with_reverse", dict(flags=8 | 4 | 2), ERR_UNSUP),
+    ("keep_with_zoh", dict(flags=8 | 4 | 1), ERR_UNSUP),
+    ("keep_with_conv", dict(flags=8 | 4, conv_width=4, conv_w=fake(22), dconv_w=fake(24)),
+     ERR_UNSUP),
     # the forward's part state is reusable only where both run the default plan
     ("reuse_with_zoh", dict(flags=4 | 1), ERR_UNSUP),
     ("reuse_with_conv", dict(flags=4, conv_width=4, conv_w=fake(22), dconv_w=fake(24)),
@@ -296,7 +307,7 @@ def test_bwd_ex_refuses_reuse_under_forced_plan(monkeypatch, plan):
     backward cannot read its part state from it."""
     monkeypatch.setenv("SELSCAN_FORCE_PLAN", plan)
     L = ss.lib()
-    for flags in (4, 4 | 2):
+    for flags in (4, 4 | 2, 8 | 4):
         assert L.selscan_bwd_ex(*bwd_ex_args(flags=flags)) == ERR_UNSUP
         assert L.selscan_last_hip_error() == 0
 
@@ -320,6 +331,21 @@ def test_flag_constants_match_header():
     assert ss.SELSCAN_FLAG_ZOH_EXACT == header_constant("SELSCAN_FLAG_ZOH_EXACT")
     assert ss.SELSCAN_FLAG_REVERSE == header_constant("SELSCAN_FLAG_REVERSE")
     assert ss.SELSCAN_FLAG_REUSE_FWD_STATE == header_constant("SELSCAN_FLAG_REUSE_FWD_STATE")
+    assert ss.SELSCAN_FLAG_KEEP_CHECKPOINTS == header_constant("SELSCAN_FLAG_KEEP_CHECKPOINTS")
+
+
+@no_gpu_only
+def test_fwd_ex_keep_checkpoints_needs_a_backward_workspace():
+    """Keeping the checkpoints writes them where the backward's layout has
+    them: a forward-sized workspace is refused before any launch."""
+    L = ss.lib()
+    fwd_bytes = L.selscan_fwd_workspace_bytes(2, 64, 128, 16, 1)
+    bwd_bytes = L.selscan_bwd_workspace_bytes(2, 64, 128, 16, 1)
+    assert 0 < fwd_bytes < bwd_bytes
+    assert L.selscan_fwd_ex(*fwd_ex_args(flags=8, workspace_bytes=fwd_bytes)) == ERR_WS
+    assert L.selscan_fwd_ex(*fwd_ex_args(flags=8, workspace_bytes=bwd_bytes - 1)) == ERR_WS
+    assert L.selscan_fwd_ex(*fwd_ex_args(flags=8, workspace=None)) == ERR_WS
+    assert L.selscan_last_hip_error() == 0
 
 
 def test_workspace_size_zero_when_grids_do_not_fit():

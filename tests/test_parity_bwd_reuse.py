@@ -1,4 +1,5 @@
-"""The backward reading the forward's part state (SELSCAN_FLAG_REUSE_FWD_STATE).
+"""The backward reading the forward's part state (SELSCAN_FLAG_REUSE_FWD_STATE),
+and also its checkpoints (SELSCAN_FLAG_KEEP_CHECKPOINTS).
 
 After a forward (selscan_fwd, or selscan_fwd_ex with REVERSE alone) in a
 workspace, selscan_bwd_ex with the flag in that workspace skips the forward's
@@ -13,12 +14,16 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import selscan_inputs as si
 import selective_state_space_selscan_amd as ss
+from parity_util import TOL, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
 REV, REUSE = ss.SELSCAN_FLAG_REVERSE, ss.SELSCAN_FLAG_REUSE_FWD_STATE
+KEEP = ss.SELSCAN_FLAG_KEEP_CHECKPOINTS
+ORACLE_NAME = {"ddelta_bias": "dbias"}
 NAMES = ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0")
 
 
@@ -93,3 +98,75 @@ def test_reuse_needs_the_forward_workspace(device):
     dy = torch.zeros_like(t["u"])
     with pytest.raises(ValueError):
         ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, flags=REUSE)
+
+
+@pytest.mark.parametrize("N", [4, 16, 64])
+@pytest.mark.parametrize("shape,dtype,parts", CASES,
+                         ids=["%dx%dx%d-%s-%s" % (c[0] + (c[1], c[2])) for c in CASES])
+def test_bwd_with_kept_checkpoints(device, monkeypatch, N, shape, dtype, parts):
+    """The forward keeps the checkpoints (y and h_last bit for bit those of
+    the plain forward) and the backward reads them with the part state: every
+    gradient against the oracle."""
+    if parts:
+        monkeypatch.setenv("SELSCAN_STREAM_PARTS", str(parts))
+    batch, L, dim = shape
+    if batch * L * dim * N > 40_000_000:
+        L = 40_000_000 // (batch * dim * N)
+    say("case keep", N, (batch, L, dim), dtype, parts)
+    inp = si.make_fwd_inputs(batch, L, dim, N, dtype, True, seed=1810 + L + N, h0=True)
+    t = si.fwd_tensors(inp, device)
+    rng = np.random.default_rng([1811, L, N])
+    dy = torch.from_numpy(rng.standard_normal((batch, L, dim)).astype(np.float32)).to(device)
+    dy = dy.to(t["u"].dtype)
+    dhl = torch.from_numpy(rng.standard_normal((batch, dim, N)).astype(np.float32)).to(device)
+    code = ss.SELSCAN_BF16 if dtype == si.BF16 else ss.SELSCAN_F32
+    ws = torch.empty(ss.selscan_bwd_workspace_bytes(batch, L, dim, N, code), dtype=torch.uint8,
+                     device=device)
+    args = (t["u"], t["delta"], t["A"], t["Bm"], t["Cm"])
+    y_keep, h_keep = ss.selscan_fwd_ex(*args, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"],
+                                       return_last_state=True, flags=KEEP, workspace=ws)
+    g = ss.selscan_bwd_ex(*args, dy, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"], dhl,
+                          flags=REUSE | KEEP, workspace=ws)
+    y, h = ss.selscan_fwd(*args, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"],
+                          return_last_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_keep, y) and torch.equal(h_keep, h)
+    ref = oracle.bwd(inp.u.value, inp.delta.value, inp.A, inp.Bm.value, inp.Cm.value,
+                     to_np(dy), inp.D_skip, inp.z.value, inp.delta_bias, True, inp.h0, to_np(dhl))
+    tol = TOL[dtype]
+    errs = {k: rel_err(to_np(g[k]), ref[ORACLE_NAME.get(k, k)]) for k in NAMES}
+    say("  rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()) + " (tol %.1g)" % tol)
+    assert all(e <= tol for e in errs.values()), errs
+
+
+def test_kept_checkpoints_on_the_layer_workload(device):
+    """The bench's training-step pair with the checkpoints kept: the
+    gradients against those of the backward that recomputes everything
+    (both within rounding of the exact gradients)."""
+    w = si.WORKLOADS["mamba130m_layer"]
+    inp = si.workload_fwd_inputs(w)
+    t = si.fwd_tensors(inp, device)
+    dy = torch.randn((w.batch, w.L, w.dim), device=device,
+                     generator=torch.Generator(device=device).manual_seed(1812)).to(t["u"].dtype)
+    ws = torch.empty(ss.selscan_bwd_workspace_bytes(w.batch, w.L, w.dim, w.N, ss.SELSCAN_BF16),
+                     dtype=torch.uint8, device=device)
+    args = (t["u"], t["delta"], t["A"], t["Bm"], t["Cm"])
+    ss.selscan_fwd_ex(*args, t["D_skip"], t["z"], t["delta_bias"], True, None, flags=KEEP,
+                      workspace=ws)
+    g_keep = ss.selscan_bwd_ex(*args, dy, t["D_skip"], t["z"], t["delta_bias"], True, None,
+                               None, flags=REUSE | KEEP, workspace=ws)
+    g_own = ss.selscan_bwd(*args, dy, t["D_skip"], t["z"], t["delta_bias"], True, None, None)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        if g_own[k] is None:
+            continue
+        e = rel_err(to_np(g_keep[k]), to_np(g_own[k]))
+        say("  %s rel_err %.2g bitwise %s" % (k, e, torch.equal(g_keep[k], g_own[k])))
+        assert e <= TOL["bf16"], (k, e)
+
+
+def test_keep_needs_a_backward_workspace(device):
+    inp = si.make_fwd_inputs(1, 64, 64, 16, si.F32, True, seed=1813)
+    t = si.fwd_tensors(inp, device)
+    with pytest.raises(ValueError):
+        ss.selscan_fwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], flags=KEEP)
