@@ -484,8 +484,8 @@ def bench_bwd(w, args):
     if pair and (vconv or vflags & ~ss.SELSCAN_FLAG_REVERSE):
         raise SystemExit("bench.py: --pass fwdbwd runs the plain path or 'rev' alone")
     keep = bool(getattr(args, "keep_checkpoints", False))
-    if keep and (not pair or vflags):
-        raise SystemExit("bench.py: --keep-checkpoints goes with --pass fwdbwd, plain path")
+    if keep and (not pair or vflags & ~ss.SELSCAN_FLAG_REVERSE):
+        raise SystemExit("bench.py: --keep-checkpoints goes with --pass fwdbwd, plain or 'rev'")
     kflag = ss.SELSCAN_FLAG_KEEP_CHECKPOINTS if keep else 0
     y = torch.empty_like(t["u"])
 

@@ -231,7 +231,7 @@ int selscan_fwd_noalloc(const void *u, const void *delta, const float *A,
  * Selective-scan forward with variants.  Arguments as selscan_fwd, plus:
  *
  *   flags        0 or an OR of SELSCAN_FLAG_ZOH_EXACT, SELSCAN_FLAG_REVERSE; or
- *                SELSCAN_FLAG_KEEP_CHECKPOINTS alone (below).
+ *                SELSCAN_FLAG_KEEP_CHECKPOINTS, alone or with REVERSE (below).
  *                ZOH_EXACT: the state update is
  *                  h = exp(Delta A) h + (exp(Delta A) - 1) / A * B u
  *                instead of h = exp(Delta A) h + Delta B u (the limit Delta B u
@@ -254,11 +254,12 @@ int selscan_fwd_noalloc(const void *u, const void *delta, const float *A,
  * With flags = 0 and conv_width = 0 this is the default forward itself (the
  * results of selscan_fwd bit for bit).
  *
- * SELSCAN_FLAG_KEEP_CHECKPOINTS (alone: with another flag bit or
+ * SELSCAN_FLAG_KEEP_CHECKPOINTS (alone or with REVERSE: with ZOH_EXACT or
  * conv_width > 0, SELSCAN_ERR_UNSUPPORTED): the forward of a training step
  * whose backward reuses this workspace (selscan_bwd_ex with
- * SELSCAN_FLAG_REUSE_FWD_STATE | SELSCAN_FLAG_KEEP_CHECKPOINTS).  The main
- * pass also stores the state entering every 4-step chunk, the checkpoints
+ * SELSCAN_FLAG_REUSE_FWD_STATE | SELSCAN_FLAG_KEEP_CHECKPOINTS and the same
+ * REVERSE flag).  The main pass also stores the state entering every 4-step
+ * chunk of the scan, the checkpoints
  * that backward's recomputation would otherwise walk the sequence for: 4 N
  * bytes per element (the paper walkthrough (m.lqnn.cn) §5.4: with memory to
  * spare, recompute less).  The workspace must then hold
@@ -372,9 +373,9 @@ int selscan_bwd(const void *u, const void *delta, const float *A,
  * cannot check the correspondence: it is the caller's to keep.  A workspace
  * of selscan_bwd_workspace_bytes is large enough for the forward too.
  *
- * SELSCAN_FLAG_KEEP_CHECKPOINTS (with SELSCAN_FLAG_REUSE_FWD_STATE and no
- * other flag bit, conv_width = 0; SELSCAN_ERR_UNSUPPORTED otherwise): that
- * forward was the plain one run with SELSCAN_FLAG_KEEP_CHECKPOINTS, and the
+ * SELSCAN_FLAG_KEEP_CHECKPOINTS (with SELSCAN_FLAG_REUSE_FWD_STATE, so plain
+ * or with REVERSE alone; SELSCAN_ERR_UNSUPPORTED without the reuse): that
+ * forward was run with SELSCAN_FLAG_KEEP_CHECKPOINTS as well, and the
  * workspace also holds its checkpoint states; the backward reads them and
  * skips its own checkpoint pass (and the forward entry states it needs).
  * The gradients are within rounding of the call without the flag (the

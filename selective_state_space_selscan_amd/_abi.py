@@ -200,7 +200,8 @@ def selscan_fwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: to
                    stream: Optional[torch.cuda.Stream] = None):
     """Forward with variants through ``selscan_fwd_ex``: ``flags`` is an OR of
     SELSCAN_FLAG_ZOH_EXACT and SELSCAN_FLAG_REVERSE, or
-    SELSCAN_FLAG_KEEP_CHECKPOINTS alone (the backward's checkpoints kept in
+    SELSCAN_FLAG_KEEP_CHECKPOINTS, alone or with REVERSE (the backward's
+    checkpoints kept in
     ``workspace``, which must then be given, of at least
     selscan_bwd_workspace_bytes); ``conv_weight`` (dim, k) float32 with k <= 4
     (and ``conv_bias`` (dim,)) enables the causal conv1d + SiLU prologue on u.
@@ -309,7 +310,7 @@ def selscan_bwd_ex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: to
     same inputs, h0 and sizes, at least ``selscan_bwd_workspace_bytes``
     long; the backward then reads that forward's part summaries and entry
     states instead of recomputing them (same result, bit for bit).  With
-    SELSCAN_FLAG_KEEP_CHECKPOINTS as well (plain only), that forward was
+    SELSCAN_FLAG_KEEP_CHECKPOINTS as well, that forward was
     ``selscan_fwd_ex`` with SELSCAN_FLAG_KEEP_CHECKPOINTS, and its kept
     checkpoint states replace the backward's checkpoint pass (the same
     gradients up to rounding)."""

@@ -366,10 +366,11 @@ hipError_t launch_fwd_summaries_ext(const FwdArgs &a, const FwdExt &e, const Str
 
 hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream)
 {
-    // no variant: the default forward itself (same plan, same bits), or with
-    // the backward's checkpoints kept (the flag comes alone)
-    if (e.flags == kFwdFlagKeepCheckpoints && e.conv_k == 0)
-        return launch_fwd_stream_keep(a, stream);
+    // the backward's checkpoints kept: the plain forward or reverse alone
+    if ((e.flags & kFwdFlagKeepCheckpoints) != 0 && e.conv_k == 0 &&
+        (e.flags & ~(kFwdFlagKeepCheckpoints | kFwdFlagReverse)) == 0)
+        return launch_fwd_stream_keep(a, (e.flags & kFwdFlagReverse) != 0, stream);
+    // no variant: the default forward itself (same plan, same bits)
     if (e.flags == 0 && e.conv_k == 0)
         return launch_fwd_stream(a, stream);
     const bool zoh = (e.flags & kFwdFlagZohExact) != 0;

@@ -72,9 +72,10 @@ static_assert(TT <= kStreamTT, "plan rounds parts to kStreamTT steps");
 // the reverse-only call then compiles to the default's code with the
 // addressing mirrored.  kVarUf (backward only): the scan input is fp32 bits
 // whatever the I/O type (the conv prologue's output, computed beforehand).
-// kVarKeep (the default forward's main pass only): the pass also stores the
-// state entering every TT-step chunk, the checkpoints a backward that reuses
-// this forward's workspace would otherwise recompute.
+// kVarKeep (the main pass of the default forward, alone or with kVarRev):
+// the pass also stores the state entering every TT-step chunk (in scan
+// order), the checkpoints a backward that reuses this forward's workspace
+// would otherwise recompute.
 enum : int { kVarExt = 1, kVarZoh = 2, kVarConv = 4, kVarRev = 8, kVarUf = 16, kVarKeep = 32 };
 constexpr int kMaxConv = 4;
 
@@ -831,7 +832,7 @@ hipError_t launch_n(const FwdArgs &a, const ExtParams &ext, const StreamPlan &p,
                        a.delta_softplus, a.h0, a.h_last, summ,                                    \
                        (const float *)(p.parts > kFoldInKernelMaxParts ? entry : nullptr), a.L,   \
                        a.dim, p.groups, p.parts, p.part_len, ext)
-    if constexpr ((VAR & ~kVarKeep) == 0 || VAR == kVarRev) {
+    if constexpr ((VAR & ~kVarKeep) == 0 || (VAR & ~kVarKeep) == kVarRev) {
         const int fx = 1 + (a.z ? 2 : 0) + (a.delta_softplus ? 1 : 0);
         if (fx == 4) SELSCAN_MAIN(4); else if (fx == 3) SELSCAN_MAIN(3);
         else if (fx == 2) SELSCAN_MAIN(2); else SELSCAN_MAIN(1);

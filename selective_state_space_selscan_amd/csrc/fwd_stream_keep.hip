@@ -1,4 +1,5 @@
-// The default forward whose main pass also keeps the backward's checkpoints:
+// The default forward (or the reverse-alone one) whose main pass also keeps
+// the backward's checkpoints:
 // the state entering every 4-step chunk, stored where a backward that reuses
 // this workspace (SELSCAN_FLAG_REUSE_FWD_STATE with
 // SELSCAN_FLAG_KEEP_CHECKPOINTS) reads them instead of recomputing them in its
@@ -14,11 +15,10 @@ namespace selscan {
 
 namespace {
 
-template <typename TIO>
+template <int V, typename TIO>
 hipError_t launch_keep(const FwdArgs &a, const StreamPlan &p, float *summ, float *entry,
                        const stream::ExtParams &x, hipStream_t s)
 {
-    constexpr int V = stream::kVarKeep;
     switch (a.N) {
     case 4: return stream::launch_n<4, V, TIO>(a, x, p, summ, entry, s);
     case 8: return stream::launch_n<8, V, TIO>(a, x, p, summ, entry, s);
@@ -31,7 +31,7 @@ hipError_t launch_keep(const FwdArgs &a, const StreamPlan &p, float *summ, float
 
 } // namespace
 
-hipError_t launch_fwd_stream_keep(const FwdArgs &a, hipStream_t stream)
+hipError_t launch_fwd_stream_keep(const FwdArgs &a, bool reverse, hipStream_t stream)
 {
     const StreamPlan p = default_fwd_plan(a.batch, a.L, a.dim);
     float *summ = stream::summary_buffer(a.workspace);   // the workspace aligned to 256 B
@@ -39,8 +39,16 @@ hipError_t launch_fwd_stream_keep(const FwdArgs &a, hipStream_t stream)
     stream::ExtParams x{};
     x.ckpt = (float *)((char *)summ + bwd_checkpoint_offset(a.batch, a.L, a.dim, a.N));
     x.nck = (a.L + stream::TT - 1) / stream::TT;
-    return a.dtype == 1 ? launch_keep<uint16_t>(a, p, summ, entry, x, stream)
-                        : launch_keep<float>(a, p, summ, entry, x, stream);
+    x.rev = reverse ? 1 : 0;
+    if (reverse) {
+        // the reverse-alone forward's code (kVarRev), checkpoints in scan order
+        constexpr int V = stream::kVarKeep | stream::kVarRev;
+        return a.dtype == 1 ? launch_keep<V, uint16_t>(a, p, summ, entry, x, stream)
+                            : launch_keep<V, float>(a, p, summ, entry, x, stream);
+    }
+    constexpr int V = stream::kVarKeep;
+    return a.dtype == 1 ? launch_keep<V, uint16_t>(a, p, summ, entry, x, stream)
+                        : launch_keep<V, float>(a, p, summ, entry, x, stream);
 }
 
 } // namespace selscan

@@ -98,9 +98,10 @@ struct FwdExt {
     int conv_k;           // 0 = no conv prologue, else 1..4
 };
 hipError_t launch_fwd_stream_ext(const FwdArgs &a, const FwdExt &e, hipStream_t stream);
-// The default forward with kFwdFlagKeepCheckpoints (fwd_stream_keep.hip); its
-// workspace is a backward's (bwd_workspace_bytes).
-hipError_t launch_fwd_stream_keep(const FwdArgs &a, hipStream_t stream);
+// The default forward (reverse: the reverse-alone one) with
+// kFwdFlagKeepCheckpoints (fwd_stream_keep.hip); its workspace is a
+// backward's (bwd_workspace_bytes).
+hipError_t launch_fwd_stream_keep(const FwdArgs &a, bool reverse, hipStream_t stream);
 // Byte offset of the checkpoint buffer in the backward's workspace layout,
 // from the workspace aligned up to 256 bytes.
 size_t bwd_checkpoint_offset(int64_t batch, int64_t L, int64_t dim, int64_t N);

@@ -398,9 +398,9 @@ int selscan_fwd_ex(const void *u, const void *delta, const float *A, const void 
         return SELSCAN_ERR_SHAPE;
     if (conv_width > SELSCAN_MAX_CONV_WIDTH)
         return SELSCAN_ERR_UNSUPPORTED;
-    // the checkpoints are kept by the plain forward alone
+    // the checkpoints are kept by the plain forward or reverse alone
     const bool keep = (flags & SELSCAN_FLAG_KEEP_CHECKPOINTS) != 0;
-    if (keep && (flags != SELSCAN_FLAG_KEEP_CHECKPOINTS || conv_width > 0))
+    if (keep && ((flags & SELSCAN_FLAG_ZOH_EXACT) || conv_width > 0))
         return SELSCAN_ERR_UNSUPPORTED;
     selscan::FwdExt e;
     e.flags = (flags & SELSCAN_FLAG_ZOH_EXACT ? selscan::kFwdFlagZohExact : 0) |
@@ -451,9 +451,9 @@ int selscan_bwd_ex(const void *u, const void *delta, const float *A, const void 
     if (flags & ~(SELSCAN_FLAG_ZOH_EXACT | SELSCAN_FLAG_REVERSE | SELSCAN_FLAG_REUSE_FWD_STATE |
                   SELSCAN_FLAG_KEEP_CHECKPOINTS))
         return SELSCAN_ERR_UNSUPPORTED;
-    // kept checkpoints come from the plain forward, read with its part state
-    if ((flags & SELSCAN_FLAG_KEEP_CHECKPOINTS) &&
-        flags != (SELSCAN_FLAG_KEEP_CHECKPOINTS | SELSCAN_FLAG_REUSE_FWD_STATE))
+    // kept checkpoints are read with the forward's part state (plain or
+    // reverse alone: the ZOH and conv cases are refused with the reuse below)
+    if ((flags & SELSCAN_FLAG_KEEP_CHECKPOINTS) && !(flags & SELSCAN_FLAG_REUSE_FWD_STATE))
         return SELSCAN_ERR_UNSUPPORTED;
     if (conv_width < 0)
         return SELSCAN_ERR_SHAPE;

@@ -157,9 +157,9 @@ def fwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, **kw):
 INVALID_FWD_EX = [
     ("unknown_flag", dict(flags=4), ERR_UNSUP),
     ("unknown_flag_16", dict(flags=16), ERR_UNSUP),
-    # the plain forward alone keeps the backward's checkpoints
-    ("keep_with_reverse", dict(flags=8 | 2), ERR_UNSUP),
+    # the plain forward or reverse alone keeps the backward's checkpoints
     ("keep_with_zoh", dict(flags=8 | 1), ERR_UNSUP),
+    ("keep_with_zoh_reverse", dict(flags=8 | 2 | 1), ERR_UNSUP),
     ("keep_with_conv", dict(flags=8, conv_width=4, conv_w=fake(13)), ERR_UNSUP),
     ("negative_flag", dict(flags=-1), ERR_UNSUP),
     ("conv_width_5", dict(conv_width=5, conv_w=fake(13)), ERR_UNSUP),
@@ -259,9 +259,9 @@ def bwd_ex_args(flags=0, conv_w=None, conv_b=None, conv_width=0, dconv_w=None, d
 
 INVALID_BWD_EX = [
     ("unknown_flag", dict(flags=16), ERR_UNSUP),
-    # kept checkpoints are read with the plain forward's part state only
+    # kept checkpoints are read with the forward's part state (plain or reverse)
     ("keep_without_reuse", dict(flags=8), ERR_UNSUP),
-    ("keep_with_reverse", dict(flags=8 | 4 | 2), ERR_UNSUP),
+    ("keep_reverse_without_reuse", dict(flags=8 | 2), ERR_UNSUP),
     ("keep_with_zoh", dict(flags=8 | 4 | 1), ERR_UNSUP),
     ("keep_with_conv", dict(flags=8 | 4, conv_width=4, conv_w=fake(22), dconv_w=fake(24)),
      ERR_UNSUP),
@@ -345,6 +345,7 @@ def test_fwd_ex_keep_checkpoints_needs_a_backward_workspace():
     assert L.selscan_fwd_ex(*fwd_ex_args(flags=8, workspace_bytes=fwd_bytes)) == ERR_WS
     assert L.selscan_fwd_ex(*fwd_ex_args(flags=8, workspace_bytes=bwd_bytes - 1)) == ERR_WS
     assert L.selscan_fwd_ex(*fwd_ex_args(flags=8, workspace=None)) == ERR_WS
+    assert L.selscan_fwd_ex(*fwd_ex_args(flags=8 | 2, workspace_bytes=fwd_bytes)) == ERR_WS
     assert L.selscan_last_hip_error() == 0
 
 

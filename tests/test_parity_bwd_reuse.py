@@ -100,10 +100,11 @@ def test_reuse_needs_the_forward_workspace(device):
         ss.selscan_bwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, flags=REUSE)
 
 
+@pytest.mark.parametrize("flags", [0, REV], ids=["plain", "reverse"])
 @pytest.mark.parametrize("N", [4, 16, 64])
 @pytest.mark.parametrize("shape,dtype,parts", CASES,
                          ids=["%dx%dx%d-%s-%s" % (c[0] + (c[1], c[2])) for c in CASES])
-def test_bwd_with_kept_checkpoints(device, monkeypatch, N, shape, dtype, parts):
+def test_bwd_with_kept_checkpoints(device, monkeypatch, flags, N, shape, dtype, parts):
     """The forward keeps the checkpoints (y and h_last bit for bit those of
     the plain forward) and the backward reads them with the part state: every
     gradient against the oracle."""
@@ -112,7 +113,7 @@ def test_bwd_with_kept_checkpoints(device, monkeypatch, N, shape, dtype, parts):
     batch, L, dim = shape
     if batch * L * dim * N > 40_000_000:
         L = 40_000_000 // (batch * dim * N)
-    say("case keep", N, (batch, L, dim), dtype, parts)
+    say("case keep", flags, N, (batch, L, dim), dtype, parts)
     inp = si.make_fwd_inputs(batch, L, dim, N, dtype, True, seed=1810 + L + N, h0=True)
     t = si.fwd_tensors(inp, device)
     rng = np.random.default_rng([1811, L, N])
@@ -124,15 +125,16 @@ def test_bwd_with_kept_checkpoints(device, monkeypatch, N, shape, dtype, parts):
                      device=device)
     args = (t["u"], t["delta"], t["A"], t["Bm"], t["Cm"])
     y_keep, h_keep = ss.selscan_fwd_ex(*args, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"],
-                                       return_last_state=True, flags=KEEP, workspace=ws)
+                                       return_last_state=True, flags=flags | KEEP, workspace=ws)
     g = ss.selscan_bwd_ex(*args, dy, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"], dhl,
-                          flags=REUSE | KEEP, workspace=ws)
-    y, h = ss.selscan_fwd(*args, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"],
-                          return_last_state=True)
+                          flags=flags | REUSE | KEEP, workspace=ws)
+    y, h = ss.selscan_fwd_ex(*args, t["D_skip"], t["z"], t["delta_bias"], True, t["h0"],
+                             return_last_state=True, flags=flags)
     torch.cuda.synchronize()
     assert torch.equal(y_keep, y) and torch.equal(h_keep, h)
     ref = oracle.bwd(inp.u.value, inp.delta.value, inp.A, inp.Bm.value, inp.Cm.value,
-                     to_np(dy), inp.D_skip, inp.z.value, inp.delta_bias, True, inp.h0, to_np(dhl))
+                     to_np(dy), inp.D_skip, inp.z.value, inp.delta_bias, True, inp.h0, to_np(dhl),
+                     flags=flags)
     tol = TOL[dtype]
     errs = {k: rel_err(to_np(g[k]), ref[ORACLE_NAME.get(k, k)]) for k in NAMES}
     say("  rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()) + " (tol %.1g)" % tol)
