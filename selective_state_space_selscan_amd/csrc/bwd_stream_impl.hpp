@@ -646,7 +646,7 @@ struct Tree {
 // steps from the last to the first.
 template <int N, bool POW, int VAR, typename TIO>
 __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, const TIO *Cm,
-                                          const WaveCtx &c, int64_t t0, const float *ck,
+                                          const WaveCtx &c, int64_t t0, const float (&ck)[N],
                                           const float (&A2)[N], const float (&invA)[N],
                                           float (&g)[N], float (&dA)[N], BwdAcc &acc, bool gated,
                                           const BwdOut &o, int64_t grp_in_row, int64_t batch,
@@ -684,7 +684,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdChunk &ch, const TIO *Bm, con
         float h[N];
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            h[n] = ck[n * kLanes];
+            h[n] = ck[n];
 #pragma unroll
         for (int i = 0; i < TT; ++i) {
             RowRaw<N, TIO> brow;
@@ -824,8 +824,16 @@ __device__ __forceinline__ void bwd_part(const UType<VAR, TIO> *u, const TIO *de
     BwdChunk A, B;
     load_bwd_chunk<VAR, SCALAR_SOFF>(A, u, delta, z, dy, c, t0, true, c.l_begin);
     for (;;) {
+        // the chunk's checkpoint first: its loads then complete before the
+        // next chunk's (loads complete in order), which stay in flight
+        float hck[N];
+        const float *ckc = ck + (t0 / TT) * (N * kLanes);
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            hck[n] = ckc[n * kLanes];
+        __builtin_amdgcn_sched_barrier(0);
         load_bwd_chunk<VAR, SCALAR_SOFF>(B, u, delta, z, dy, c, t0 - TT, true, c.l_begin);
-        bwd_chunk<N, POW, VAR>(A, Bm, Cm, c, t0, ck + (t0 / TT) * (N * kLanes), A2, invA, g, dA,
+        bwd_chunk<N, POW, VAR>(A, Bm, Cm, c, t0, hck, A2, invA, g, dA,
                                acc, gated, o, grp_in_row, batch, lane, active);
         t0 -= TT;
         if (t0 < c.l_begin)
