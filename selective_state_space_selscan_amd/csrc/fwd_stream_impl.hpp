@@ -922,12 +922,15 @@ hipError_t launch_ext(const FwdArgs &a, const FwdExt &e, hipStream_t s)
     if (!x.rev)
         return bf ? launch_ext_fixed<N, ZOH, uint16_t>(a, x, p, summ, entry, s)
                   : launch_ext_fixed<N, ZOH, float>(a, x, p, summ, entry, s);
-    constexpr int V = kVarExt | (ZOH ? kVarZoh : 0);
+    // reverse with the conv prologue or exact ZOH: the direction fixed at
+    // compile time as well (kVarRev; the softplus switch and the gate chosen
+    // per launch, as in the forward-direction variants)
+    constexpr int VR = kVarRev | (ZOH ? kVarZoh : 0);
     if (e.conv_k > 0)
-        return bf ? launch_n<N, V | kVarConv, uint16_t>(a, x, p, summ, entry, s)
-                  : launch_n<N, V | kVarConv, float>(a, x, p, summ, entry, s);
-    return bf ? launch_n<N, V, uint16_t>(a, x, p, summ, entry, s)
-              : launch_n<N, V, float>(a, x, p, summ, entry, s);
+        return bf ? launch_n<N, VR | kVarConv, uint16_t>(a, x, p, summ, entry, s)
+                  : launch_n<N, VR | kVarConv, float>(a, x, p, summ, entry, s);
+    return bf ? launch_n<N, VR, uint16_t>(a, x, p, summ, entry, s)
+              : launch_n<N, VR, float>(a, x, p, summ, entry, s);
 }
 
 } // namespace stream
