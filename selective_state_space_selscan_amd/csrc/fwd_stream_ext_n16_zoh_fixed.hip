@@ -2,7 +2,7 @@
 // exact zero-order hold B_bar in the forward direction, direction and softplus switch
 // fixed at compile time (launch_ext_fixed): the conv1d + SiLU prologue, and the scan without it.
 // A unit of its own so that it compiles in parallel with the
-// run-time-direction variants of fwd_stream_ext_n16_zoh.hip.
+// reverse-direction variants of fwd_stream_ext_n16_zoh.hip.
 #include "fwd_stream_impl.hpp"
 
 namespace selscan {

@@ -2,7 +2,7 @@
 // B_bar = Delta B in the forward direction, direction and softplus switch
 // fixed at compile time (launch_ext_fixed): the conv1d + SiLU prologue.
 // A unit of its own so that it compiles in parallel with the
-// run-time-direction variants of fwd_stream_ext_n32.hip.
+// reverse-direction variants of fwd_stream_ext_n32.hip.
 #include "fwd_stream_impl.hpp"
 
 namespace selscan {

@@ -1,7 +1,8 @@
 // Variant instantiations of the streaming forward for state size N = 4 with
-// exact zero-order hold B_bar: the variants with REVERSE (the direction a run-time
-// flag) and the summary pass the variants' backward uses; the
-// forward-direction variants are in the matching _fixed unit.  One
+// exact zero-order hold B_bar: the variants with REVERSE (the direction fixed
+// at compile time) and the summary pass the variants' backward uses (the
+// direction a run-time flag); the forward-direction variants are in the
+// matching _fixed unit.  One
 // translation unit per (N, B_bar form) so that they compile in parallel.
 #include "fwd_stream_impl.hpp"
 

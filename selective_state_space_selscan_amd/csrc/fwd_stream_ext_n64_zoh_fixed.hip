@@ -3,7 +3,7 @@
 // fixed at compile time (launch_ext_fixed): the conv1d + SiLU prologue, and the scan without it;
 // bf16 I/O (fp32 I/O: fwd_stream_ext_n64_zoh_fixed_f32.hip).
 // A unit of its own so that it compiles in parallel with the
-// run-time-direction variants of fwd_stream_ext_n64_zoh.hip.
+// reverse-direction variants of fwd_stream_ext_n64_zoh.hip.
 #include "fwd_stream_impl.hpp"
 
 namespace selscan {

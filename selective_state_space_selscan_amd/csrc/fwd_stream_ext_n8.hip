@@ -1,7 +1,8 @@
 // Variant instantiations of the streaming forward for state size N = 8 with
-// B_bar = Delta B: the variants with REVERSE (the direction a run-time
-// flag), reverse alone, and the summary pass the variants' backward uses; the
-// forward-direction variants are in the matching _fixed unit.  One
+// B_bar = Delta B: the variants with REVERSE (the direction fixed at compile
+// time), reverse alone, and the summary pass the variants' backward uses (the
+// direction a run-time flag); the forward-direction variants are in the
+// matching _fixed unit.  One
 // translation unit per (N, B_bar form) so that they compile in parallel.
 #include "fwd_stream_impl.hpp"
 

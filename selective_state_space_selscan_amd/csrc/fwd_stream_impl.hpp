@@ -880,7 +880,7 @@ hipError_t launch_ext_summaries(const FwdArgs &a, const FwdExt &e, const StreamP
 // softplus switch fixed at compile time (conv, ZOH, ZOH + conv; the plain
 // case is the default forward).  Instantiated explicitly in the
 // fwd_stream_ext_n*_fixed.hip units, so that they compile in parallel with
-// the run-time-direction ones.
+// the reverse-direction ones.
 template <int N, bool ZOH, typename TIO>
 hipError_t launch_ext_fixed(const FwdArgs &a, const ExtParams &x, const StreamPlan &p,
                             float *summ, float *entry, hipStream_t s)
