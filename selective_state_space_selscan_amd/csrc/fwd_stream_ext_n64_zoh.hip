@@ -15,6 +15,14 @@ extern template hipError_t launch_ext_fixed<64, true, uint16_t>(const FwdArgs &,
 extern template hipError_t launch_ext_fixed<64, true, float>(const FwdArgs &, const ExtParams &,
                                                          const StreamPlan &, float *, float *,
                                                          hipStream_t);
+// compiled in fwd_stream_ext_n64_zoh_rev_f32.hip: the reverse variants with
+// fp32 I/O
+extern template hipError_t launch_n<64, kVarRev | kVarZoh, float>(const FwdArgs &,
+                                                                 const ExtParams &,
+                                                                 const StreamPlan &, float *,
+                                                                 float *, hipStream_t);
+extern template hipError_t launch_n<64, kVarRev | kVarZoh | kVarConv, float>(
+    const FwdArgs &, const ExtParams &, const StreamPlan &, float *, float *, hipStream_t);
 } // namespace stream
 
 hipError_t launch_fwd_stream_ext_n64_zoh(const FwdArgs &a, const FwdExt &e, hipStream_t stream)
