@@ -139,21 +139,27 @@ def test_ex_without_variants_matches_fwd(device):
     assert torch.equal(y0, y1) and torch.equal(h0, h1)
 
 
+@pytest.mark.parametrize("N,dim", [(4, 96), (16, 192), (32, 96), (64, 64)])
 @pytest.mark.parametrize("dtype", [si.F32, si.BF16])
-@pytest.mark.parametrize("conv", [False, True])
-def test_reverse_is_forward_on_flipped_sequence_bitwise(device, dtype, conv):
+@pytest.mark.parametrize("zoh,conv", [(True, False), (True, True), (False, True)])
+def test_reverse_is_forward_on_flipped_sequence_bitwise(device, N, dim, dtype, zoh, conv):
     """REVERSE walks the same scan-order arithmetic over flipped addresses, so
-    it equals the forward variant on the flipped inputs bit for bit."""
-    inp = si.make_fwd_inputs(2, 1234, 192, 16, dtype, True, seed=1000, h0=True)
+    it equals the forward variant on the flipped inputs bit for bit.  With
+    exact ZOH, the conv prologue or both, the reverse and the forward
+    direction are separate instantiations (each direction fixed at compile
+    time), for every state size."""
+    inp = si.make_fwd_inputs(2, 1234, dim, N, dtype, True, seed=1000 + N, h0=True)
     t = si.fwd_tensors(inp, device)
-    cw = torch.from_numpy(si.conv_params(192, 4, 1001)[0]).to(device) if conv else None
+    cw = torch.from_numpy(si.conv_params(dim, 4, 1001)[0]).to(device) if conv else None
+    flags = ZOH if zoh else 0
+    print("case reverse flip N", N, "dim", dim, dtype, "zoh", zoh, "conv", conv, flush=True)
     f = lambda x: x.flip(1).contiguous()
     y_r, h_r = ss.selscan_fwd_ex(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D_skip"],
                                  t["z"], t["delta_bias"], True, t["h0"], return_last_state=True,
-                                 flags=REV | ZOH, conv_weight=cw)
+                                 flags=REV | flags, conv_weight=cw)
     y_f, h_f = ss.selscan_fwd_ex(f(t["u"]), f(t["delta"]), t["A"], f(t["Bm"]), f(t["Cm"]),
                                  t["D_skip"], f(t["z"]), t["delta_bias"], True, t["h0"],
-                                 return_last_state=True, flags=ZOH, conv_weight=cw)
+                                 return_last_state=True, flags=flags, conv_weight=cw)
     torch.cuda.synchronize()
     assert torch.equal(y_r, f(y_f)) and torch.equal(h_r, h_f)
 
