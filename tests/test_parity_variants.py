@@ -114,13 +114,18 @@ def test_variants_ragged(device, shape):
     check_ex(inp, device, REV, si.conv_params(dim, 3, 702, False), what="ragged")
 
 
-def test_variants_without_softplus(device):
-    """delta_softplus = 0: Delta = Delta_raw + bias, here kept positive."""
-    inp = si.make_fwd_inputs(2, 600, 96, 16, si.F32, True, seed=800, h0=True)
+@pytest.mark.parametrize("flags,conv_k", [(ZOH | REV, 4), (REV, 4), (ZOH | REV, 0), (ZOH, 0),
+                                          (0, 4), (ZOH, 4)])
+@pytest.mark.parametrize("gate", [True, False])
+def test_variants_without_softplus(device, flags, conv_k, gate):
+    """delta_softplus = 0: Delta = Delta_raw + bias, here kept positive; with
+    and without the gate, in both directions (the softplus switch and the
+    gate are chosen per launch in every variant instantiation)."""
+    inp = si.make_fwd_inputs(2, 600, 96, 16, si.F32, gate, seed=800 + flags + conv_k, h0=True)
     inp.delta.value[:] = np.abs(inp.delta.value) * 0.05
     inp.delta_bias = np.full(96, 1e-3, np.float32)
-    check_ex(inp, device, ZOH | REV, si.conv_params(96, 4, 801), softplus=False,
-             what="no_softplus")
+    conv = si.conv_params(96, conv_k, 801) if conv_k else None
+    check_ex(inp, device, flags, conv, softplus=False, what="no_softplus")
 
 
 def test_ex_without_variants_matches_fwd(device):
